@@ -1,0 +1,202 @@
+#!/usr/bin/env python3
+"""Benchmark: RMSNorm-training backward at [131072, 4096] BF16 on one MI355X.
+
+A step is one backward call (dx + dw; main kernel + FP64 fold) of the
+non-deterministic mode at T = 131072, H = 4096, x / dy BF16 ~ N(0,1),
+w FP32 = 1 + 0.1 N(0,1), eps = 1e-6, inputs resident in HBM. Reported:
+whole-call throughput in algorithmic GB/s, us/call, the deterministic mode
+and the forward on the same shape, the HBM roofline of the call, and the FP64
+CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+One GPU only: --gpus N with N > 1 exits with a message.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
+T_HEAD, H_HEAD = 131072, 4096
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_131072x4096.json")
+KERNEL_SOURCES = ["rmsn_kernels.hpp", "rmsn_device.hpp", "rmsn_bwd_large.hip"]
+
+
+def bwd_bytes(T, H, w_bytes):
+    # read x, dy (2 B each), write dx (2 B) per element; rstd 4T; w; dw 4H
+    return 6 * T * H + 4 * T + w_bytes * H + 4 * H
+
+
+def fwd_bytes(T, H, w_bytes):
+    return 4 * T * H + 4 * T + w_bytes * H
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "rmsnorm_train_fwd_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per call from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != kernel_hash():
+        return None
+    return t.get("bytes_per_call")
+
+
+def time_calls(fn, steps, warmup, torch):
+    """Per-call HIP-event times (ms) on the current stream, and wall ms per call."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    ev = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return ev, wall
+
+
+def cpu_baseline(p, rows_sample):
+    """The FP64 oracle (single-threaded C) on the first rows of the workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    W = p.width
+    xs = p.x.view(-1, W)[:rows_sample].contiguous().view(torch.int16).numpy().view(np.uint16)
+    dys = p.dy.view(-1, W)[:rows_sample].contiguous().view(torch.int16).numpy().view(np.uint16)
+    w64 = p.w.double().numpy()
+    t0 = time.perf_counter()
+    oracle.bwd(oracle.View.dense(dys), oracle.View.dense(xs), w64, p.eps)
+    dt = time.perf_counter() - t0
+    gbps = bwd_bytes(rows_sample, W, 4) / dt / 1e9
+    return {
+        "value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"backward (dx and dw) of the first {rows_sample} of {p.T} rows, width {W}, "
+                  f"{dt:.2f} s, same algorithmic byte model as value",
+        "us_per_call_scaled": round(dt * 1e6 * p.T / rows_sample, 1),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=16384)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by rows with one dw all-reduce; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import rmsnorm_train_fwd_amd as R
+    from rmsnorm_train_fwd_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating inputs [{T_HEAD}, {H_HEAD}]", file=sys.stderr, flush=True)
+    p = synth.make(T_HEAD, H_HEAD, seed=0, w_dtype="f32")
+    x = p.x.to(dev).view(T_HEAD, H_HEAD)
+    dy = p.dy.to(dev).view(T_HEAD, H_HEAD)
+    w = p.w.to(dev)
+    y, rstd = R.rmsnorm_train_fwd(x, w, p.eps)
+    plan_nd = R.rmsnorm_train_bwd_query(x, False)
+    plan_d = R.rmsnorm_train_bwd_query(x, True)
+    ws = torch.empty(max(plan_nd.workspace_bytes, plan_d.workspace_bytes), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+
+    def bwd_nd():
+        R.rmsnorm_train_bwd(dy, x, rstd, w, False, workspace=ws)
+
+    def bwd_d():
+        R.rmsnorm_train_bwd(dy, x, rstd, w, True, workspace=ws)
+
+    def fwd():
+        R.rmsnorm_train_fwd(x, w, p.eps)
+
+    print("[bench] timing backward (non-deterministic)", file=sys.stderr, flush=True)
+    ev, wall = time_calls(bwd_nd, args.steps, args.warmup, torch)
+    print("[bench] timing backward (deterministic) and forward", file=sys.stderr, flush=True)
+    ev_d, _ = time_calls(bwd_d, max(10, args.steps // 2), 3, torch)
+    ev_f, _ = time_calls(fwd, max(10, args.steps // 2), 3, torch)
+
+    def med(v):
+        return v[len(v) // 2]
+
+    mean_ms = sum(ev) / len(ev)
+    nbytes = bwd_bytes(T_HEAD, H_HEAD, 4)
+    gbps = nbytes / (mean_ms * 1e-3) / 1e9
+    traffic = measured_traffic()
+    result = {
+        "metric": "bwd us/call and achieved HBM GB/s (% of peak) at [131072,4096] BF16",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: x, dy ~ N(0,1) cast to BF16, w = 1 + 0.1 N(0,1) FP32, seed 0",
+        "config": {
+            "workload": "rmsnorm_train_bwd non-deterministic, x/dy/dx BF16 [131072, 4096], "
+                        "w FP32, dw FP32, eps 1e-6",
+            "T": T_HEAD, "H": H_HEAD, "w_dtype": "f32", "deterministic": False,
+            "algorithmic_bytes_per_call": nbytes,
+            "workspace_bytes": plan_nd.workspace_bytes,
+        },
+        "us_per_call": {"mean": round(mean_ms * 1e3, 2), "median": round(med(ev) * 1e3, 2),
+                        "p10": round(ev[len(ev) // 10] * 1e3, 2),
+                        "p90": round(ev[(9 * len(ev)) // 10] * 1e3, 2)},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "backward call: k_bwd_large + k_fold (HIP events around each call)",
+            "achieved": round(gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+        },
+        "extra": {
+            "bwd_det_us": round(med(ev_d) * 1e3, 2),
+            "bwd_det_GBps": round(bwd_bytes(T_HEAD, H_HEAD, 4) / (med(ev_d) * 1e-3) / 1e9, 1),
+            "fwd_us": round(med(ev_f) * 1e3, 2),
+            "fwd_GBps": round(fwd_bytes(T_HEAD, H_HEAD, 4) / (med(ev_f) * 1e-3) / 1e9, 1),
+        },
+    }
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(p, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

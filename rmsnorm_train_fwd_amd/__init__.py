@@ -1,0 +1,269 @@
+"""RMSNorm for training on MI355X (gfx950): Python binding of librmsnorm_train.so.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/rmsnorm_train.h. PyTorch supplies
+device memory and the current HIP stream. There is no fallback: if the library
+is not built, or a tensor is not on a ROCm device, the call raises.
+
+Names follow the C ABI:
+  rmsnorm_train_fwd(x, w, eps, residual=None)        -> y, rstd[, h]
+  rmsnorm_train_bwd(dy, x, rstd, w, deterministic, dh=None) -> dx | grad_h, dw
+  rmsnorm_train_bwd_query(shape..., deterministic)   -> plan (host only)
+  rmsnorm_silu_gate_train_fwd(x, z, w, eps)          -> y, rstd
+  rmsnorm_silu_gate_train_bwd(dy, x, z, rstd, w, deterministic) -> dx, dz, dw
+Row tensors are BF16 [T, H] (one row per token) or [T, heads, width] views
+whose last dimension is contiguous; w is [width] BF16 or FP32.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librmsnorm_train.so")
+
+RMSN_BF16, RMSN_F32 = 0, 1
+PATH_AUTO, PATH_SMALL, PATH_LARGE = 0, 1, 2
+STATUS = {
+    0: "RMSN_OK", 1: "RMSN_E_NULL", 2: "RMSN_E_DTYPE", 3: "RMSN_E_SHAPE", 4: "RMSN_E_STRIDE",
+    5: "RMSN_E_ALIGN", 6: "RMSN_E_ALIAS", 7: "RMSN_E_WORKSPACE", 8: "RMSN_E_LAUNCH",
+    9: "RMSN_E_ARG", 10: "RMSN_E_HIP",
+}
+EXPORTS = (
+    "rmsnorm_train_fwd", "rmsnorm_train_bwd", "rmsnorm_train_bwd_query",
+    "rmsnorm_silu_gate_train_fwd", "rmsnorm_silu_gate_train_bwd", "rmsn_status_str",
+)
+
+
+class Layout(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in
+                ("T", "heads", "width", "x_stride_t", "x_stride_h", "g_stride_t", "g_stride_h")]
+
+
+class Launch(C.Structure):
+    _fields_ = [("grid", C.c_int32), ("fold_grid", C.c_int32), ("path", C.c_int32)]
+
+
+class BwdPlan(C.Structure):
+    _fields_ = [
+        ("path", C.c_int32), ("rows", C.c_int64), ("chunk_rows", C.c_int64),
+        ("chunks", C.c_int64), ("subchains", C.c_int32), ("fold_group", C.c_int32),
+        ("grid", C.c_int32), ("fold_grid", C.c_int32), ("workspace_bytes", C.c_size_t),
+    ]
+
+
+class RmsnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        self.status = STATUS.get(code, str(code))
+        super().__init__(f"{where}: {self.status} ({lib().rmsn_status_str(code).decode()})")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m rmsnorm_train_fwd_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        vp, lp, lap, fp = C.c_void_p, C.POINTER(Layout), C.POINTER(Launch), C.c_float
+        L.rmsnorm_train_fwd.argtypes = [vp, vp, vp, C.c_int, fp, lp, vp, vp, vp, vp]
+        L.rmsnorm_train_bwd.argtypes = [vp, vp, vp, vp, C.c_int, vp, C.c_int, lp, vp, vp, vp,
+                                        C.c_size_t, lap, vp]
+        L.rmsnorm_train_bwd_query.argtypes = [lp, C.c_int, lap, C.POINTER(BwdPlan)]
+        L.rmsnorm_silu_gate_train_fwd.argtypes = [vp, vp, vp, C.c_int, fp, lp, vp, vp, vp]
+        L.rmsnorm_silu_gate_train_bwd.argtypes = [vp, vp, vp, vp, C.c_int, vp, C.c_int, lp, vp,
+                                                  vp, vp, vp, C.c_size_t, lap, vp]
+        for name in EXPORTS[:-1]:
+            getattr(L, name).restype = C.c_int
+        L.rmsn_status_str.argtypes = [C.c_int]
+        L.rmsn_status_str.restype = C.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise RmsnError(code, where)
+
+
+# --------------------------------------------------------------- marshalling --
+
+def _geometry(t: torch.Tensor, name: str):
+    """(T, heads, width, stride_t, stride_h) of a [T, H] or [T, heads, width] tensor."""
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dim() == 2:
+        T, W = t.shape
+        return (T, 1, W, t.stride(0) if T > 1 else W, W)
+    if t.dim() == 3:
+        T, H, W = t.shape
+        return (T, H, W, t.stride(0) if T > 1 else H * W, t.stride(1) if H > 1 else W)
+    raise ValueError(f"{name} must be 2-D [T, H] or 3-D [T, heads, width]")
+
+
+def _inner_contiguous(t: torch.Tensor, name: str):
+    if t.numel() and t.stride(-1) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+
+
+def _device(t: torch.Tensor, name: str):
+    if t.device.type != "cuda":
+        raise RuntimeError(f"{name} must be on a ROCm GPU device (no CPU path exists)")
+
+
+def _layout(x: torch.Tensor, g: Optional[torch.Tensor]) -> Layout:
+    gx = _geometry(x, "x")
+    gg = _geometry(g, "dy") if g is not None else gx
+    if gx[:3] != gg[:3]:
+        raise ValueError(f"shape mismatch: {tuple(x.shape)} vs {tuple(g.shape)}")
+    return Layout(gx[0], gx[1], gx[2], gx[3], gx[4], gg[3], gg[4])
+
+
+def _same_geometry(a: torch.Tensor, b: torch.Tensor, an: str, bn: str):
+    if _geometry(a, an) != _geometry(b, bn):
+        raise ValueError(f"{bn} must have the shape and strides of {an}")
+
+
+def _w(w: torch.Tensor, width: int):
+    if w.dim() != 1 or w.shape[0] != width or not w.is_contiguous():
+        raise ValueError(f"w must be a contiguous [{width}] vector")
+    if w.dtype == torch.bfloat16:
+        return RMSN_BF16
+    if w.dtype == torch.float32:
+        return RMSN_F32
+    raise TypeError(f"w must be bfloat16 or float32, got {w.dtype}")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr() or None
+
+
+def _launch(grid=0, fold_grid=0, path=PATH_AUTO) -> Launch:
+    return Launch(grid, fold_grid, path)
+
+
+def _rows_shape(x: torch.Tensor):
+    return tuple(x.shape), tuple(x.shape[:-1])
+
+
+# -------------------------------------------------------------------- calls --
+
+def rmsnorm_train_fwd(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
+                      residual: Optional[torch.Tensor] = None):
+    """y = RMSNorm(x) * w (BF16) and rstd (FP32). With a residual: h = x + residual
+    (BF16) is normalised and returned as well: (y, rstd, h)."""
+    _device(x, "x")
+    _inner_contiguous(x, "x")
+    L = _layout(x, None)
+    wd = _w(w, L.width)
+    if residual is not None:
+        _same_geometry(x, residual, "x", "residual")
+    full, rows = _rows_shape(x)
+    y = torch.empty(full, dtype=torch.bfloat16, device=x.device)
+    rstd = torch.empty(rows, dtype=torch.float32, device=x.device)
+    h = torch.empty(full, dtype=torch.bfloat16, device=x.device) if residual is not None else None
+    _check(lib().rmsnorm_train_fwd(_ptr(x), _ptr(residual), _ptr(w), wd, float(eps), C.byref(L),
+                                   _ptr(y), _ptr(h), _ptr(rstd), _stream(x)), "rmsnorm_train_fwd")
+    return (y, rstd) if h is None else (y, rstd, h)
+
+
+def rmsnorm_train_bwd_query(x: torch.Tensor, deterministic: bool = True,
+                            launch: Optional[Launch] = None, dy: Optional[torch.Tensor] = None):
+    L = _layout(x, dy)
+    plan = BwdPlan()
+    _check(lib().rmsnorm_train_bwd_query(C.byref(L), int(bool(deterministic)),
+                                         C.byref(launch) if launch else None, C.byref(plan)),
+           "rmsnorm_train_bwd_query")
+    return plan
+
+
+def _workspace(plan: BwdPlan, x: torch.Tensor, workspace: Optional[torch.Tensor]):
+    if plan.workspace_bytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=x.device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def rmsnorm_train_bwd(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor, w: torch.Tensor,
+                      deterministic: bool = True, dh: Optional[torch.Tensor] = None,
+                      launch: Optional[Launch] = None, workspace: Optional[torch.Tensor] = None):
+    """dx (BF16) and dw (FP32). With dh (residual form; x is then the forward's
+    BF16 h): grad_h = dh + dx replaces dx."""
+    for t, n in ((dy, "dy"), (x, "x"), (rstd, "rstd")):
+        _device(t, n)
+    _inner_contiguous(x, "x")
+    _inner_contiguous(dy, "dy")
+    L = _layout(x, dy)
+    wd = _w(w, L.width)
+    if dh is not None:
+        _same_geometry(dy, dh, "dy", "dh")
+    if rstd.dtype != torch.float32 or rstd.numel() != L.T * L.heads or not rstd.is_contiguous():
+        raise ValueError("rstd must be a contiguous float32 tensor with one value per row")
+    plan = rmsnorm_train_bwd_query(x, deterministic, launch, dy)
+    ws, ws_bytes = _workspace(plan, x, workspace)
+    full, _ = _rows_shape(x)
+    dx = torch.empty(full, dtype=torch.bfloat16, device=x.device)
+    dw = torch.empty(L.width, dtype=torch.float32, device=x.device)
+    _check(lib().rmsnorm_train_bwd(_ptr(dy), _ptr(x), _ptr(dh), _ptr(w), wd, _ptr(rstd),
+                                   int(bool(deterministic)), C.byref(L), _ptr(dx), _ptr(dw),
+                                   _ptr(ws), ws_bytes, C.byref(launch) if launch else None,
+                                   _stream(x)), "rmsnorm_train_bwd")
+    return dx, dw
+
+
+def rmsnorm_silu_gate_train_fwd(x: torch.Tensor, z: torch.Tensor, w: torch.Tensor,
+                                eps: float = 1e-6):
+    """y = RMSNorm(x) * w * silu(z) (BF16) and rstd (FP32)."""
+    _device(x, "x")
+    _inner_contiguous(x, "x")
+    _same_geometry(x, z, "x", "z")
+    L = _layout(x, None)
+    wd = _w(w, L.width)
+    full, rows = _rows_shape(x)
+    y = torch.empty(full, dtype=torch.bfloat16, device=x.device)
+    rstd = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check(lib().rmsnorm_silu_gate_train_fwd(_ptr(x), _ptr(z), _ptr(w), wd, float(eps), C.byref(L),
+                                             _ptr(y), _ptr(rstd), _stream(x)),
+           "rmsnorm_silu_gate_train_fwd")
+    return y, rstd
+
+
+def rmsnorm_silu_gate_train_bwd(dy: torch.Tensor, x: torch.Tensor, z: torch.Tensor,
+                                rstd: torch.Tensor, w: torch.Tensor, deterministic: bool = True,
+                                launch: Optional[Launch] = None,
+                                workspace: Optional[torch.Tensor] = None):
+    """dx, dz (BF16) and dw (FP32) of the SiLU-gated form."""
+    for t, n in ((dy, "dy"), (x, "x"), (z, "z"), (rstd, "rstd")):
+        _device(t, n)
+    _inner_contiguous(x, "x")
+    _inner_contiguous(dy, "dy")
+    _same_geometry(x, z, "x", "z")
+    L = _layout(x, dy)
+    wd = _w(w, L.width)
+    if rstd.dtype != torch.float32 or rstd.numel() != L.T * L.heads or not rstd.is_contiguous():
+        raise ValueError("rstd must be a contiguous float32 tensor with one value per row")
+    plan = rmsnorm_train_bwd_query(x, deterministic, launch, dy)
+    ws, ws_bytes = _workspace(plan, x, workspace)
+    full, _ = _rows_shape(x)
+    dx = torch.empty(full, dtype=torch.bfloat16, device=x.device)
+    dz = torch.empty(full, dtype=torch.bfloat16, device=x.device)
+    dw = torch.empty(L.width, dtype=torch.float32, device=x.device)
+    _check(lib().rmsnorm_silu_gate_train_bwd(_ptr(dy), _ptr(x), _ptr(z), _ptr(w), wd, _ptr(rstd),
+                                             int(bool(deterministic)), C.byref(L), _ptr(dx),
+                                             _ptr(dz), _ptr(dw), _ptr(ws), ws_bytes,
+                                             C.byref(launch) if launch else None, _stream(x)),
+           "rmsnorm_silu_gate_train_bwd")
+    return dx, dz, dw

@@ -1,0 +1,52 @@
+// rmsn_bwd_small.hip -- single-launch small-row backward instances and launcher.
+#include "rmsn_kernels.hpp"
+
+namespace rmsn {
+
+namespace {
+template <int H, bool WF32>
+hipError_t small_form(int form, const BwdArgs& a, int row_grid, int col_grid, hipStream_t s) {
+  const int grid = row_grid + col_grid;
+  switch (form) {
+    case kPlain: k_bwd_small<H, WF32, kPlain><<<grid, kBlock, 0, s>>>(a, row_grid); break;
+    case kResidual: k_bwd_small<H, WF32, kResidual><<<grid, kBlock, 0, s>>>(a, row_grid); break;
+    case kGate: k_bwd_small<H, WF32, kGate><<<grid, kBlock, 0, s>>>(a, row_grid); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int H>
+hipError_t small_width(bool w_f32, int form, const BwdArgs& a, int rg, int cg, hipStream_t s) {
+  return w_f32 ? small_form<H, true>(form, a, rg, cg, s) : small_form<H, false>(form, a, rg, cg, s);
+}
+}  // namespace
+
+int bwd_rows_per_rowtask(int H) {
+  switch (H) {
+    case 256: return Geo<256>::R;
+    case 512: return Geo<512>::R;
+    case 1536: return Geo<1536>::R;
+    case 2048: return Geo<2048>::R;
+    case 4096: return Geo<4096>::R;
+    case 5120: return Geo<5120>::R;
+    case 6144: return Geo<6144>::R;
+    default: return 0;
+  }
+}
+
+hipError_t launch_bwd_small(int H, bool w_f32, int form, const BwdArgs& a, int row_grid,
+                            int col_grid, hipStream_t s) {
+  switch (H) {
+    case 256: return small_width<256>(w_f32, form, a, row_grid, col_grid, s);
+    case 512: return small_width<512>(w_f32, form, a, row_grid, col_grid, s);
+    case 1536: return small_width<1536>(w_f32, form, a, row_grid, col_grid, s);
+    case 2048: return small_width<2048>(w_f32, form, a, row_grid, col_grid, s);
+    case 4096: return small_width<4096>(w_f32, form, a, row_grid, col_grid, s);
+    case 5120: return small_width<5120>(w_f32, form, a, row_grid, col_grid, s);
+    case 6144: return small_width<6144>(w_f32, form, a, row_grid, col_grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace rmsn

@@ -1,0 +1,250 @@
+// rmsn_device.hpp -- device building blocks of the gfx950 RMSNorm-training kernels.
+//
+// Compiled for gfx950 only (wave64). All translation units that include this
+// header build with -ffp-contract=off and without fast-math: the error-free
+// transforms below (TwoSum, TwoProduct) are exact only if the compiler keeps
+// every rounding where it is written. FP32 denormals are preserved (HIP's
+// default), since TwoProduct error terms can be subnormal.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rmsn {
+
+typedef uint16_t u16;
+typedef uint32_t u32;
+
+// ----------------------------------------------------------------- formats --
+
+// BF16 element 2i of a packed pair sits in the low half of 32-bit word i.
+__device__ __forceinline__ float bf_lo(u32 w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(u32 w) { return __uint_as_float(w & 0xffff0000u); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two FP32 values -> packed BF16 pair, round to nearest even
+// (one v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(u32, __builtin_convertvector(v, bf16x2_t));
+}
+
+// 8 BF16 values (one 16-byte vector) <-> 8 floats.
+__device__ __forceinline__ void unpack8(const uint4& u, float (&f)[8]) {
+  f[0] = bf_lo(u.x); f[1] = bf_hi(u.x);
+  f[2] = bf_lo(u.y); f[3] = bf_hi(u.y);
+  f[4] = bf_lo(u.z); f[5] = bf_hi(u.z);
+  f[6] = bf_lo(u.w); f[7] = bf_hi(u.w);
+}
+
+__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
+  uint4 u;
+  u.x = pack_bf16x2(f[0], f[1]);
+  u.y = pack_bf16x2(f[2], f[3]);
+  u.z = pack_bf16x2(f[4], f[5]);
+  u.w = pack_bf16x2(f[6], f[7]);
+  return u;
+}
+
+__device__ __forceinline__ uint4 ld16(const u16* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Streaming loads/stores: data touched exactly once per call.
+typedef u32 u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const u16* p) {
+  u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st16_stream(u16* p, const uint4& v) {
+  u32x4_t t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t*>(p));
+}
+
+// --------------------------------------------------- error-free transforms --
+
+// Knuth's TwoSum: s + e == a + b exactly (no magnitude precondition).
+__device__ __forceinline__ void two_sum(float a, float b, float& s, float& e) {
+  s = a + b;
+  float bb = s - a;
+  e = (a - (s - bb)) + (b - bb);
+}
+
+// TwoProduct by FMA: p + e == a * b exactly (barring underflow).
+__device__ __forceinline__ void two_prod(float a, float b, float& p, float& e) {
+  p = a * b;
+  e = __builtin_fmaf(a, b, -p);
+}
+
+// ------------------------------------------------------- cross-lane sums --
+//
+// Butterfly sums inside a wave. Every lane ends with the same bits: each step
+// adds a lane's value to its partner's, and IEEE addition is commutative.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_partner_add(float v) {
+  int p = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false);
+  return v + __int_as_float(p);
+}
+
+// Sum over the 16 lanes of each DPP row.
+__device__ __forceinline__ float sum16(float v) {
+  v = dpp_partner_add<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  v = dpp_partner_add<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  v = dpp_partner_add<0x141>(v);  // row_half_mirror: quad 0 <-> quad 1 of each 8
+  v = dpp_partner_add<0x140>(v);  // row_mirror: half-row 0 <-> half-row 1
+  return v;
+}
+
+// Sum over each half-wave (lanes 0-31 and 32-63 separately).
+__device__ __forceinline__ float sum32(float v) {
+  v = sum16(v);
+  // v_permlane16_swap with both operands = v: one result holds the even rows,
+  // the other the odd rows, so their sum is row(2k) + row(2k+1) in every lane.
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over the whole wave.
+__device__ __forceinline__ float sum64(float v) {
+  v = sum32(v);
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int LANES>
+__device__ __forceinline__ float lane_sum(float v) {
+  static_assert(LANES == 32 || LANES == 64, "row groups are half or whole waves");
+  if constexpr (LANES == 32) return sum32(v);
+  else return sum64(v);
+}
+
+// ------------------------------------------------------ per-width layout --
+//
+// A row of `H` BF16 elements is handled by a row group of TPR threads; each
+// thread owns V 16-byte vectors (8 elements each): vector v of lane l covers
+// elements (v*TPR + l)*8 .. +7, so one load instruction of the row group
+// reads TPR*16 contiguous bytes. A 256-thread workgroup holds R = 256/TPR
+// row groups, which work on R different rows at a time.
+template <int H> struct Cfg;
+template <> struct Cfg<256>  { static constexpr int TPR = 32,  V = 1; };
+template <> struct Cfg<512>  { static constexpr int TPR = 64,  V = 1; };
+template <> struct Cfg<1536> { static constexpr int TPR = 64,  V = 3; };
+template <> struct Cfg<2048> { static constexpr int TPR = 128, V = 2; };
+template <> struct Cfg<4096> { static constexpr int TPR = 256, V = 2; };
+template <> struct Cfg<5120> { static constexpr int TPR = 128, V = 5; };
+template <> struct Cfg<6144> { static constexpr int TPR = 256, V = 3; };
+
+constexpr int kBlock = 256;
+
+template <int H>
+struct Geo {
+  static constexpr int TPR = Cfg<H>::TPR;
+  static constexpr int V = Cfg<H>::V;
+  static constexpr int R = kBlock / TPR;           // row groups per workgroup
+  static constexpr int LANES = TPR < 64 ? TPR : 64;
+  static constexpr int WPR = TPR / LANES;          // waves per row group
+  static constexpr int E = 8 * V;                  // elements per thread
+  static_assert(TPR * V * 8 == H, "layout must tile the row exactly");
+};
+
+// Weight in registers: the E elements a thread owns, as FP32.
+template <int H, bool WF32>
+__device__ __forceinline__ void load_w(const void* w, int lane, float (&wr)[Geo<H>::E]) {
+  constexpr int TPR = Geo<H>::TPR;
+#pragma unroll
+  for (int v = 0; v < Geo<H>::V; ++v) {
+    const int e0 = (v * TPR + lane) * 8;
+    if constexpr (WF32) {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(w) + e0);
+      float4 a = p[0], b = p[1];
+      wr[v * 8 + 0] = a.x; wr[v * 8 + 1] = a.y; wr[v * 8 + 2] = a.z; wr[v * 8 + 3] = a.w;
+      wr[v * 8 + 4] = b.x; wr[v * 8 + 5] = b.y; wr[v * 8 + 6] = b.z; wr[v * 8 + 7] = b.w;
+    } else {
+      float f[8];
+      unpack8(ld16(static_cast<const u16*>(w) + e0), f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wr[v * 8 + i] = f[i];
+    }
+  }
+}
+
+// Sum of D per-thread partials over each row group; every thread of the row
+// group receives the totals. Row groups of one or half a wave use lane sums
+// only. Wider row groups add the per-wave sums through LDS in wave order
+// ((w0 + w1) + w2) + ..., with two alternating slot sets so that one barrier
+// per call suffices. All threads of the workgroup must call it together.
+template <int H, int D>
+struct RowSum {
+  static constexpr int R = Geo<H>::R, WPR = Geo<H>::WPR;
+  static constexpr int kSlots = (WPR > 1) ? 2 * R * WPR * D : 1;
+
+  __device__ static void run(float (&v)[D], float* slots, int& parity, int q, int lane) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) v[d] = lane_sum<Geo<H>::LANES>(v[d]);
+    if constexpr (WPR > 1) {
+      float* s = slots + (parity * R + q) * WPR * D;
+      const int wv = lane / 64;
+      if ((lane & 63) == 0) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) s[wv * D + d] = v[d];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        float t = s[d];
+#pragma unroll
+        for (int k = 1; k < WPR; ++k) t += s[k * D + d];
+        v[d] = t;
+      }
+      parity ^= 1;
+    }
+  }
+};
+
+// ------------------------------------------------------------ dw tree --
+//
+// Deterministic dw: the rows of a call are cut into canonical chunks of C rows
+// (C from the row count alone, see the host plan); inside chunk k the rows
+// k*C + q + i*R (i = 0, 1, ...) form sub-chain q, summed in ascending order by
+// Dot2 (TwoProduct + TwoSum, compensation in FP32); the chunk partial is
+// 0.0 + d_0 + d_1 + ... + d_{R-1} in FP64 with d_q = (double)s_q + (double)c_q;
+// partials fold in FP64: consecutive groups of kFoldGroup chunks are summed in
+// ascending order from 0.0, then the group sums in ascending order from 0.0,
+// then one rounding to FP32. Every kernel below that produces dw follows this
+// tree operation for operation, so dw has the same bits on every path.
+struct Dot2 {
+  float s = 0.0f, c = 0.0f;
+  // Adds the exact product a*b (a itself exact, e.g. dy*x of two BF16 values).
+  __device__ __forceinline__ void add(float a, float b) {
+    float p, pe, t;
+    two_prod(a, b, p, pe);
+    two_sum(s, p, s, t);
+    c = c + (t + pe);
+  }
+  __device__ __forceinline__ double value() const { return (double)s + (double)c; }
+};
+
+// Non-deterministic dw: FP32 sums over blocks of 8 rows of a sub-chain, each
+// block flushed into a TwoSum-compensated pair.
+struct Block8 {
+  float b = 0.0f, s = 0.0f, c = 0.0f;
+  __device__ __forceinline__ void add(float dy, float xh) { b = __builtin_fmaf(dy, xh, b); }
+  __device__ __forceinline__ void flush() {
+    float t;
+    two_sum(s, b, s, t);
+    c = c + t;
+    b = 0.0f;
+  }
+  __device__ __forceinline__ double value() const { return (double)s + (double)c; }
+};
+
+// SiLU pieces in FP32: sigmoid by the hardware exp2 and reciprocal
+// (v_exp_f32, v_rcp_f32; about 1 ulp each). Large negative z gives
+// exp2 -> +inf and sigmoid -> 0; large positive z gives sigmoid -> 1.
+__device__ __forceinline__ float sigmoid_f(float z) {
+  float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
+  return __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+}  // namespace rmsn

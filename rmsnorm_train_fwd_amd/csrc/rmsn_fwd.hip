@@ -1,0 +1,52 @@
+// rmsn_fwd.hip -- forward kernel instances and their launcher.
+#include "rmsn_kernels.hpp"
+
+namespace rmsn {
+
+namespace {
+constexpr int kFwdRPG = 2;  // rows per row group per tile
+
+template <int H, bool WF32>
+hipError_t fwd_form(int form, const FwdArgs& a, int grid, hipStream_t s) {
+  switch (form) {
+    case kPlain: k_fwd<H, WF32, kPlain, kFwdRPG><<<grid, kBlock, 0, s>>>(a); break;
+    case kResidual: k_fwd<H, WF32, kResidual, kFwdRPG><<<grid, kBlock, 0, s>>>(a); break;
+    case kGate: k_fwd<H, WF32, kGate, kFwdRPG><<<grid, kBlock, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int H>
+hipError_t fwd_width(bool w_f32, int form, const FwdArgs& a, int grid, hipStream_t s) {
+  return w_f32 ? fwd_form<H, true>(form, a, grid, s) : fwd_form<H, false>(form, a, grid, s);
+}
+}  // namespace
+
+int fwd_rows_per_tile(int H) {
+  switch (H) {
+    case 256: return Geo<256>::R * kFwdRPG;
+    case 512: return Geo<512>::R * kFwdRPG;
+    case 1536: return Geo<1536>::R * kFwdRPG;
+    case 2048: return Geo<2048>::R * kFwdRPG;
+    case 4096: return Geo<4096>::R * kFwdRPG;
+    case 5120: return Geo<5120>::R * kFwdRPG;
+    case 6144: return Geo<6144>::R * kFwdRPG;
+    default: return 0;
+  }
+}
+
+hipError_t launch_fwd(int H, bool w_f32, int form, const FwdArgs& a, int grid, hipStream_t s) {
+  switch (H) {
+    case 256: return fwd_width<256>(w_f32, form, a, grid, s);
+    case 512: return fwd_width<512>(w_f32, form, a, grid, s);
+    case 1536: return fwd_width<1536>(w_f32, form, a, grid, s);
+    case 2048: return fwd_width<2048>(w_f32, form, a, grid, s);
+    case 4096: return fwd_width<4096>(w_f32, form, a, grid, s);
+    case 5120: return fwd_width<5120>(w_f32, form, a, grid, s);
+    case 6144: return fwd_width<6144>(w_f32, form, a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace rmsn

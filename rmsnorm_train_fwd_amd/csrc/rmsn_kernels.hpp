@@ -1,0 +1,425 @@
+// rmsn_kernels.hpp -- the gfx950 kernels of RMSNorm training.
+//
+//   k_fwd        forward: y, rstd (+ h for the fused residual, silu gate)
+//   k_bwd_large  backward main kernel: dx (+dz) and FP64 dw chunk partials
+//   k_fold       fixed-order FP64 fold of the chunk partials -> dw (FP32)
+//   k_bwd_small  single-launch backward for small row counts: row tasks for
+//                dx, column tasks for dw over all rows, no workspace
+//
+// What they compute is stated in include/rmsnorm_train.h. The rows are
+// streamed once from HBM with 16-byte loads; every thread keeps the weight
+// slice it needs in registers for its whole lifetime.
+#pragma once
+
+#include "rmsn_device.hpp"
+#include "rmsn_launch.hpp"
+
+namespace rmsn {
+
+__device__ __forceinline__ int64_t row_off(const RowIn& in, int64_t row, int heads) {
+  const uint32_t t = (uint32_t)row / (uint32_t)heads;
+  const uint32_t h = (uint32_t)row - t * (uint32_t)heads;
+  return (int64_t)t * in.stride_t + (int64_t)h * in.stride_h;
+}
+
+template <int H>
+__device__ __forceinline__ int elem0(int v, int lane) {
+  return (v * Geo<H>::TPR + lane) * 8;
+}
+
+// ------------------------------------------------------------------ forward --
+//
+// Per row: ss = sum x^2 (FP32, per-thread FMA chain, then the row-group sum),
+// rstd = 1/sqrt(ss/H + eps) with IEEE sqrt and division, y = bf16((x*rstd)*w)
+// [* silu(z)]. Residual: h = bf16(x + res) (FP32 sum of two BF16 values,
+// rounded once; the FP32 sum can only be inexact when the addends' exponents
+// differ by more than 16, and then the smaller one is far below half a BF16
+// ulp, so the result is the rounded exact sum), and the norm reads that h.
+template <int H, bool WF32, int FORM, int RPG>
+__global__ __launch_bounds__(kBlock) void k_fwd(FwdArgs a) {
+  using G = Geo<H>;
+  constexpr int R = G::R, V = G::V, E = G::E;
+  const int q = threadIdx.x / G::TPR, lane = threadIdx.x % G::TPR;
+  __shared__ float slots[RowSum<H, RPG>::kSlots];
+  int parity = 0;
+  float wr[E];
+  load_w<H, WF32>(a.w, lane, wr);
+
+  const int64_t tiles = (a.rows + R * RPG - 1) / (R * RPG);
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    int64_t row[RPG];
+    bool ok[RPG];
+    uint4 xv[RPG][V], ev[RPG][V];
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      row[i] = tile * (R * RPG) + i * R + q;
+      ok[i] = row[i] < a.rows;
+      const int64_t xo = ok[i] ? row_off(a.x, row[i], a.heads) : 0;
+      const int64_t eo = ok[i] && FORM != kPlain ? row_off(a.e, row[i], a.heads) : 0;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        xv[i][v] = ok[i] ? ld16_stream(a.x.p + xo + elem0<H>(v, lane)) : make_uint4(0, 0, 0, 0);
+        if constexpr (FORM != kPlain)
+          ev[i][v] = ok[i] ? ld16_stream(a.e.p + eo + elem0<H>(v, lane)) : make_uint4(0, 0, 0, 0);
+      }
+    }
+    float xf[RPG][E];
+    float ss[RPG];
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        float f[8];
+        unpack8(xv[i][v], f);
+        if constexpr (FORM == kResidual) {
+          float r8[8];
+          unpack8(ev[i][v], r8);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) f[k] = f[k] + r8[k];
+          const uint4 hb = pack8(f);
+          if (ok[i]) st16_stream(a.h + row[i] * H + elem0<H>(v, lane), hb);
+          unpack8(hb, f);  // the norm reads the rounded h
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) xf[i][v * 8 + k] = f[k];
+      }
+      float s = 0.0f;
+#pragma unroll
+      for (int k = 0; k < E; ++k) s = __builtin_fmaf(xf[i][k], xf[i][k], s);
+      ss[i] = s;
+    }
+    RowSum<H, RPG>::run(ss, slots, parity, q, lane);
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const float r = 1.0f / __builtin_sqrtf(ss[i] / (float)H + a.eps);
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        float f[8];
+        float zf[8];
+        if constexpr (FORM == kGate) unpack8(ev[i][v], zf);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          float t = (xf[i][v * 8 + k] * r) * wr[v * 8 + k];
+          if constexpr (FORM == kGate) t = t * (zf[k] * sigmoid_f(zf[k]));
+          f[k] = t;
+        }
+        if (ok[i]) st16_stream(a.y + row[i] * H + elem0<H>(v, lane), pack8(f));
+      }
+      if (ok[i] && lane == 0) a.rstd[row[i]] = r;
+    }
+  }
+}
+
+// ----------------------------------------------------------------- backward --
+//
+// One batch of D rows of one row group: loads, the row sum c = sum g*xhat,
+// dx = rstd*(g - xhat*c/H) (+dh), dz for the gate, stores. Returns the loaded
+// x, dy (and z) for the dw accumulation. The arithmetic of a row does not
+// depend on D or on the kernel calling it, so dx has the same bits on every
+// path.
+template <int H, int FORM, int D>
+struct RowBatch {
+  static constexpr int V = Geo<H>::V, E = Geo<H>::E;
+  uint4 xv[D][V], gv[D][V], ev[D][V];
+  float r[D];
+
+  __device__ __forceinline__ void load(const BwdArgs& a, const int64_t (&row)[D],
+                                       const bool (&ok)[D], int lane) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int64_t xo = ok[d] ? row_off(a.x, row[d], a.heads) : 0;
+      const int64_t go = ok[d] ? row_off(a.dy, row[d], a.heads) : 0;
+      const int64_t eo = ok[d] && FORM != kPlain ? row_off(a.e, row[d], a.heads) : 0;
+      r[d] = ok[d] ? a.rstd[row[d]] : 0.0f;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int e0 = elem0<H>(v, lane);
+        xv[d][v] = ok[d] ? ld16_stream(a.x.p + xo + e0) : make_uint4(0, 0, 0, 0);
+        gv[d][v] = ok[d] ? ld16_stream(a.dy.p + go + e0) : make_uint4(0, 0, 0, 0);
+        if constexpr (FORM != kPlain)
+          ev[d][v] = ok[d] ? ld16_stream(a.e.p + eo + e0) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+
+  template <bool WF32>
+  __device__ __forceinline__ void compute_store(const BwdArgs& a, const float (&wr)[E],
+                                                const int64_t (&row)[D], const bool (&ok)[D],
+                                                int q, int lane, float* slots, int& parity) {
+    float dot[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      float s = 0.0f;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        float xf[8], gf[8], zf[8];
+        unpack8(xv[d][v], xf);
+        unpack8(gv[d][v], gf);
+        if constexpr (FORM == kGate) unpack8(ev[d][v], zf);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          float g = gf[k] * wr[v * 8 + k];
+          if constexpr (FORM == kGate) g = g * (zf[k] * sigmoid_f(zf[k]));
+          s = __builtin_fmaf(g, xf[k] * r[d], s);
+        }
+      }
+      dot[d] = s;
+    }
+    RowSum<H, D>::run(dot, slots, parity, q, lane);
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const float c = dot[d] / (float)H;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        float xf[8], gf[8], zf[8], out[8], dz[8];
+        unpack8(xv[d][v], xf);
+        unpack8(gv[d][v], gf);
+        if constexpr (FORM != kPlain) unpack8(ev[d][v], zf);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float xh = xf[k] * r[d];
+          float g = gf[k] * wr[v * 8 + k];
+          if constexpr (FORM == kGate) {
+            const float sg = sigmoid_f(zf[k]);
+            g = g * (zf[k] * sg);
+            dz[k] = ((gf[k] * xh) * wr[v * 8 + k]) * (sg * (1.0f + zf[k] * (1.0f - sg)));
+          }
+          float dx = r[d] * __builtin_fmaf(-xh, c, g);
+          if constexpr (FORM == kResidual) dx = zf[k] + dx;  // grad_h = dh + dx
+          out[k] = dx;
+        }
+        const int64_t o = row[d] * H + elem0<H>(v, lane);
+        if (ok[d]) {
+          st16_stream(a.dx + o, pack8(out));
+          if constexpr (FORM == kGate) st16_stream(a.dz + o, pack8(dz));
+        }
+      }
+    }
+  }
+
+  // dw terms of row d, element (v, k), into a deterministic accumulator:
+  // exact a = dy*x, times rstd (or RN(rstd*silu(z)) for the gate).
+  __device__ __forceinline__ void det_terms(int d, int v, float (&a8)[8], float (&b8)[8]) const {
+    float xf[8], gf[8];
+    unpack8(xv[d][v], xf);
+    unpack8(gv[d][v], gf);
+    float zf[8];
+    if constexpr (FORM == kGate) unpack8(ev[d][v], zf);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      a8[k] = gf[k] * xf[k];
+      b8[k] = r[d];
+      if constexpr (FORM == kGate) b8[k] = r[d] * (zf[k] * sigmoid_f(zf[k]));
+    }
+  }
+
+  // dw terms for the blocked FP32 accumulator: dy and xhat (* silu).
+  __device__ __forceinline__ void blk_terms(int d, int v, float (&a8)[8], float (&b8)[8]) const {
+    float xf[8], gf[8];
+    unpack8(xv[d][v], xf);
+    unpack8(gv[d][v], gf);
+    float zf[8];
+    if constexpr (FORM == kGate) unpack8(ev[d][v], zf);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      a8[k] = gf[k];
+      b8[k] = xf[k] * r[d];
+      if constexpr (FORM == kGate) b8[k] = b8[k] * (zf[k] * sigmoid_f(zf[k]));
+    }
+  }
+};
+
+// Backward main kernel. Workgroup-strided over the canonical chunks of the dw
+// tree; inside a chunk, row group q walks rows k*C + q + i*R in ascending i,
+// D rows per batch, accumulating its sub-chain; the R sub-chains merge in
+// order through LDS in FP64 and the chunk partial goes to ws[k][:].
+template <int H, bool WF32, int FORM, bool DET, int D>
+__global__ __launch_bounds__(kBlock) void k_bwd_large(BwdArgs a) {
+  using G = Geo<H>;
+  constexpr int R = G::R, V = G::V, E = G::E, TPR = G::TPR;
+  static_assert(8 % D == 0, "a batch must not straddle an 8-row block");
+  const int q = threadIdx.x / TPR, lane = threadIdx.x % TPR;
+  __shared__ float slots[RowSum<H, D>::kSlots];
+  __shared__ double merge[R > 1 ? H : 1];
+  int parity = 0;
+  float wr[E];
+  load_w<H, WF32>(a.w, lane, wr);
+  const int64_t C = a.chunk_rows;
+  const int nb = (int)((C + R * D - 1) / (R * D));
+
+  for (int64_t k = blockIdx.x; k < a.chunks; k += gridDim.x) {
+    const int64_t r0 = k * C;
+    const int64_t r1 = r0 + C < a.rows ? r0 + C : a.rows;
+    Dot2 dacc[DET ? E : 1];
+    Block8 bacc[DET ? 1 : E];
+    for (int b = 0; b < nb; ++b) {
+      int64_t row[D];
+      bool ok[D];
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        row[d] = r0 + (int64_t)(b * D + d) * R + q;
+        ok[d] = row[d] < r1;
+      }
+      RowBatch<H, FORM, D> rb;
+      rb.load(a, row, ok, lane);
+      rb.template compute_store<WF32>(a, wr, row, ok, q, lane, slots, parity);
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        if (!ok[d]) continue;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          float a8[8], b8[8];
+          if constexpr (DET) {
+            rb.det_terms(d, v, a8, b8);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dacc[v * 8 + i].add(a8[i], b8[i]);
+          } else {
+            rb.blk_terms(d, v, a8, b8);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) bacc[v * 8 + i].add(a8[i], b8[i]);
+          }
+        }
+      }
+      if constexpr (!DET) {
+        if (((b + 1) * D) % 8 == 0) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) bacc[e].flush();
+        }
+      }
+    }
+    double dv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if constexpr (DET) {
+        dv[e] = dacc[e].value();
+      } else {
+        bacc[e].flush();
+        dv[e] = bacc[e].value();
+      }
+    }
+    double* out = a.ws + k * H;
+    if constexpr (R == 1) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        double2* o = reinterpret_cast<double2*>(out + elem0<H>(v, lane));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[i] = make_double2(0.0 + dv[v * 8 + 2 * i], 0.0 + dv[v * 8 + 2 * i + 1]);
+      }
+    } else {
+      // p = 0.0 + d_0 + d_1 + ... + d_{R-1}, in row-group order.
+      for (int qq = 0; qq < R; ++qq) {
+        if (q == qq) {
+#pragma unroll
+          for (int v = 0; v < V; ++v)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              double& m = merge[elem0<H>(v, lane) + i];
+              m = (qq == 0 ? 0.0 : m) + dv[v * 8 + i];
+            }
+        }
+        __syncthreads();
+      }
+      for (int i = threadIdx.x; i < H; i += kBlock) out[i] = merge[i];
+      __syncthreads();
+    }
+  }
+}
+
+// Fold: dw[j] = RN_fp32( sum_g ( sum_{k in group g} ws[k][j] ) ), both sums in
+// ascending order from 0.0, groups of kFoldGroup consecutive chunks. One
+// workgroup covers kColTile columns: each wave sums whole groups, wave 0 adds
+// the group sums.
+__global__ __launch_bounds__(kBlock) void k_fold(const double* __restrict__ ws,
+                                                 float* __restrict__ dw, int H, int64_t chunks);
+
+// Small-row backward in one launch. Workgroups [0, row_grid) are row tasks
+// (dx, strided over row tiles of R rows); the rest are column tasks (dw),
+// strided over tiles of kColTile columns. A column-task thread (cv, kl) owns 8
+// columns and, per pass, chunk kl of the current fold group: it runs the R
+// sub-chains of its chunk exactly as k_bwd_large does, then the fold follows
+// k_fold's order through LDS. rstd is an input, so dw needs nothing from the
+// row tasks and no workgroup ever waits for another.
+template <int H, bool WF32, int FORM>
+__global__ __launch_bounds__(kBlock) void k_bwd_small(BwdArgs a, int row_grid) {
+  using G = Geo<H>;
+  constexpr int R = G::R, TPR = G::TPR;
+  __shared__ float slots[RowSum<H, 1>::kSlots];
+  __shared__ double part[kFoldGroup][kColTile];
+  if ((int)blockIdx.x < row_grid) {
+    const int q = threadIdx.x / TPR, lane = threadIdx.x % TPR;
+    int parity = 0;
+    float wr[G::E];
+    load_w<H, WF32>(a.w, lane, wr);
+    const int64_t tiles = (a.rows + R - 1) / R;
+    for (int64_t t = blockIdx.x; t < tiles; t += row_grid) {
+      int64_t row[1] = {t * R + q};
+      bool ok[1] = {row[0] < a.rows};
+      RowBatch<H, FORM, 1> rb;
+      rb.load(a, row, ok, lane);
+      rb.template compute_store<WF32>(a, wr, row, ok, q, lane, slots, parity);
+    }
+    return;
+  }
+  constexpr int CV = kColTile / 8;            // column vectors per tile
+  constexpr int KL = kBlock / CV;             // chunk lanes
+  static_assert(KL == kFoldGroup, "one pass of chunk lanes is one fold group");
+  const int cv = threadIdx.x % CV, kl = threadIdx.x / CV;
+  const int col_grid = gridDim.x - row_grid;
+  const int64_t C = a.chunk_rows;
+  const int64_t groups = (a.chunks + kFoldGroup - 1) / kFoldGroup;
+  for (int tile = blockIdx.x - row_grid; tile < H / kColTile; tile += col_grid) {
+    const int c0 = tile * kColTile + cv * 8;
+    double total[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) total[i] = 0.0;
+    for (int64_t g = 0; g < groups; ++g) {
+      const int64_t k = g * kFoldGroup + kl;
+      if (k < a.chunks) {
+        double p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = 0.0;
+        const int64_t r0 = k * C;
+        const int64_t r1 = r0 + C < a.rows ? r0 + C : a.rows;
+        for (int qq = 0; qq < R; ++qq) {
+          Dot2 acc[8];
+          for (int64_t row = r0 + qq; row < r1; row += R) {
+            const float r = a.rstd[row];
+            float xf[8], gf[8], zf[8];
+            unpack8(ld16(a.x.p + row_off(a.x, row, a.heads) + c0), xf);
+            unpack8(ld16(a.dy.p + row_off(a.dy, row, a.heads) + c0), gf);
+            if constexpr (FORM == kGate) unpack8(ld16(a.e.p + row_off(a.e, row, a.heads) + c0), zf);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              float b = r;
+              if constexpr (FORM == kGate) b = r * (zf[i] * sigmoid_f(zf[i]));
+              acc[i].add(gf[i] * xf[i], b);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) p[i] = p[i] + acc[i].value();
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part[kl][cv * 8 + i] = p[i];
+      }
+      __syncthreads();
+      if (kl == 0) {
+        const int64_t n = a.chunks - g * kFoldGroup < kFoldGroup ? a.chunks - g * kFoldGroup : kFoldGroup;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          double s = 0.0;
+          for (int64_t kk = 0; kk < n; ++kk) s = s + part[kk][cv * 8 + i];
+          total[i] = total[i] + s;
+        }
+      }
+      __syncthreads();
+    }
+    if (kl == 0) {
+      float4* o = reinterpret_cast<float4*>(a.dw + c0);
+      o[0] = make_float4((float)total[0], (float)total[1], (float)total[2], (float)total[3]);
+      o[1] = make_float4((float)total[4], (float)total[5], (float)total[6], (float)total[7]);
+    }
+  }
+}
+
+}  // namespace rmsn

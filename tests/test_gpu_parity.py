@@ -1,0 +1,218 @@
+"""GPU parity: the HIP library against the FP64 oracle on the same seeded
+inputs, element by element (row outputs on all rows, or on a sample of rows
+at the full sizes; dw always on every column, summed over every row).
+
+Workloads are the five configurations of the build (seeded synthetic inputs,
+synth.py): [8,512] fwd+bwd; the small-row deterministic sweep incl. per-head
+[T,24,256] views; large-T non-deterministic and deterministic backward;
+fused residual at width 6144; the SiLU gate at width 4096.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rmsnorm_train_fwd_amd as R
+from rmsnorm_train_fwd_amd import synth
+
+from helpers import (TOL_DW, TOL_DX, TOL_Y, RTOL_RSTD, OnGpu, assert_within, bf16_ulp_distance,
+                     bits, oview, ratio, sample_rows, w_f64)
+
+pytestmark = pytest.mark.gpu
+
+WIDTHS = (512, 1536, 2048, 4096, 5120, 6144)
+SMALL_T = (1, 2, 4, 8, 16, 32, 64, 128, 203)
+FULL = os.environ.get("RMSN_FULL") == "1"
+
+
+def run_case(p: synth.Problem, det=True, form="plain", launch=None, nsample=None, seed=0):
+    """fwd + bwd on the GPU, checked against the oracle. Returns error ratios."""
+    g = OnGpu(p)
+    if form == "residual":
+        y, rstd, h = R.rmsnorm_train_fwd(g.x, g.w, p.eps, residual=g.e)
+        xin = h
+        dx, dw = R.rmsnorm_train_bwd(g.dy, h, rstd, g.w, det, dh=g.dh, launch=launch)
+    elif form == "gate":
+        y, rstd = R.rmsnorm_silu_gate_train_fwd(g.x, g.e, g.w, p.eps)
+        dx, dz, dw = R.rmsnorm_silu_gate_train_bwd(g.dy, g.x, g.e, rstd, g.w, det, launch=launch)
+    else:
+        y, rstd = R.rmsnorm_train_fwd(g.x, g.w, p.eps)
+        dx, dw = R.rmsnorm_train_bwd(g.dy, g.x, rstd, g.w, det, launch=launch)
+    torch.cuda.synchronize()
+
+    rows, W = p.rows, p.width
+    sel = sample_rows(rows, nsample, seed) if nsample else np.arange(rows, dtype=np.int64)
+    w64 = w_f64(p.w)
+    xo, dyo = oview(p, p.x), oview(p, p.dy)
+    out = {}
+    if form == "residual":
+        ho, yo, ro = oracle.res_fwd(xo, oview(p, p.extra), w64, p.eps, sel)
+        hg = bits(h).reshape(rows, W)
+        assert np.array_equal(hg, ho), "h = bf16(x + residual) must be bit-exact"
+        xb = oracle.View(ho, p.T, p.heads, W, p.heads * W, W)
+        rows_out, dwo = oracle.bwd(dyo, xb, w64, p.eps, dh=oview(p, p.dh), sel=sel)
+    elif form == "gate":
+        zo = oview(p, p.extra)
+        yo, ro = oracle.gate_fwd(xo, zo, w64, p.eps, sel)
+        rows_out, dzo, dwo = oracle.gate_bwd(dyo, xo, zo, w64, p.eps, sel)
+        dzg = oracle.bf16_to_f64(bits(dz).reshape(rows, W)[sel])
+        out["dz"] = assert_within(dzg, dzo, TOL_DX, "dz")
+    else:
+        yo, ro = oracle.fwd(xo, w64, p.eps, sel)
+        rows_out, dwo = oracle.bwd(dyo, xo, w64, p.eps, sel=sel)
+
+    yb = bits(y).reshape(rows, W)[sel]
+    out["y"] = assert_within(oracle.bf16_to_f64(yb), yo, TOL_Y, "y")
+    ulp = bf16_ulp_distance(yb, oracle.f64_to_bf16(yo))
+    assert ulp.max(initial=0) <= 1, f"y differs from the rounded oracle by {ulp.max()} BF16 ulp"
+    rg = rstd.reshape(-1).cpu().double().numpy()[sel]
+    out["rstd"] = assert_within(rg, ro, (0.0, RTOL_RSTD), "rstd")
+    dxg = oracle.bf16_to_f64(bits(dx).reshape(rows, W)[sel])
+    out["dx"] = assert_within(dxg, rows_out, TOL_DX, "dx" if form != "residual" else "grad_h")
+    out["dw"] = assert_within(dw.cpu().double().numpy(), dwo, TOL_DW, "dw")
+    return out
+
+
+# ------------------------------------------------------------- config 1 ---
+
+@pytest.mark.parametrize("seed", range(5))
+def test_config1_8x512_det_fwd_bwd(seed):
+    p = synth.make(8, 512, seed=seed, w_dtype="bf16")
+    run_case(p, det=True)
+
+
+# ------------------------------------------------------------- config 2 ---
+
+@pytest.mark.parametrize("w_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("H", WIDTHS)
+def test_config2_small_row_det_sweep(H, w_dtype):
+    for T in SMALL_T:
+        for seed in range(5):
+            run_case(synth.make(T, H, seed=seed, w_dtype=w_dtype), det=True)
+
+
+@pytest.mark.parametrize("strides", [(12288, 512), (6144, 256)], ids=["pages_12288_512", "dense_6144_256"])
+@pytest.mark.parametrize("w_dtype", ["f32", "bf16"])
+def test_config2_per_head_views(strides, w_dtype):
+    for T in SMALL_T:
+        for seed in range(2):
+            p = synth.make(T, 256, seed=seed, heads=24, w_dtype=w_dtype,
+                           row_stride=strides[0], head_stride=strides[1])
+            run_case(p, det=True)
+    p = synth.make(64, 256, seed=3, heads=4, w_dtype=w_dtype)  # [T,4,256] contiguous
+    run_case(p, det=True)
+    run_case(p, det=False)
+
+
+# ------------------------------------------------------------- config 3 ---
+
+@pytest.mark.parametrize("det", [False, True], ids=["nondet", "det"])
+@pytest.mark.parametrize("H", WIDTHS)
+def test_config3_large_path_elementwise_ragged(H, det):
+    # spans many chunks and a ragged last chunk, every row checked
+    run_case(synth.make(4099, H, seed=1, w_dtype="f32"), det=det)
+
+
+@pytest.mark.parametrize("det", [False, True], ids=["nondet", "det"])
+def test_config3_headline_131072x4096(det):
+    run_case(synth.make(131072, 4096, seed=0, w_dtype="f32"), det=det, nsample=64)
+
+
+@pytest.mark.parametrize("T,H", [(65537, 6144), (98304, 1536), (131072, 5120), (65537, 2048)])
+def test_config3_full_size_nondet(T, H):
+    run_case(synth.make(T, H, seed=2, w_dtype="f32"), det=False, nsample=32)
+
+
+@pytest.mark.skipif(not FULL, reason="full config-3 sweep: set RMSN_FULL=1")
+@pytest.mark.parametrize("det", [False, True], ids=["nondet", "det"])
+@pytest.mark.parametrize("T", [65537, 98304, 131072])
+@pytest.mark.parametrize("H", (1536, 2048, 4096, 5120, 6144))
+def test_config3_full_sweep(H, T, det):
+    run_case(synth.make(T, H, seed=3, w_dtype="f32"), det=det, nsample=24)
+
+
+# ------------------------------------------------------------- config 4 ---
+
+@pytest.mark.parametrize("det", [False, True], ids=["nondet", "det"])
+@pytest.mark.parametrize("w_dtype", ["f32", "bf16"])
+def test_config4_residual_6144(w_dtype, det):
+    for seed in range(3):
+        run_case(synth.make(32, 6144, seed=seed, w_dtype=w_dtype, form="residual"), det=det,
+                 form="residual")
+    run_case(synth.make(65537, 6144, seed=0, w_dtype=w_dtype, form="residual"), det=det,
+             form="residual", nsample=32)
+
+
+@pytest.mark.skipif(not FULL, reason="T=131072 residual: set RMSN_FULL=1")
+def test_config4_residual_131072():
+    run_case(synth.make(131072, 6144, seed=1, w_dtype="f32", form="residual"), det=True,
+             form="residual", nsample=24)
+
+
+# ------------------------------------------------------------- config 5 ---
+
+@pytest.mark.parametrize("det", [False, True], ids=["nondet", "det"])
+@pytest.mark.parametrize("w_dtype", ["f32", "bf16"])
+def test_config5_gate_3534x4096(w_dtype, det):
+    run_case(synth.make(3534, 4096, seed=0, w_dtype=w_dtype, form="gate"), det=det, form="gate")
+
+
+@pytest.mark.parametrize("T", [8192, 16384])
+def test_config5_gate_larger(T):
+    run_case(synth.make(T, 4096, seed=1, w_dtype="f32", form="gate"), det=False, form="gate",
+             nsample=48)
+
+
+@pytest.mark.parametrize("H", (256, 512, 1536, 2048, 5120, 6144))
+def test_gate_other_widths(H):
+    run_case(synth.make(300, H, seed=4, w_dtype="f32", form="gate"), det=True, form="gate")
+
+
+@pytest.mark.parametrize("H", (256, 512, 4096))
+def test_residual_other_widths(H):
+    run_case(synth.make(300, H, seed=4, w_dtype="bf16", form="residual"), det=True,
+             form="residual")
+
+
+# ------------------------------------------------------------ input families --
+
+@pytest.mark.parametrize("family", ["cancel", "spread"])
+@pytest.mark.parametrize("H", (512, 4096))
+def test_det_adversarial_families(H, family):
+    # deterministic dw keeps the budget on cancellation and scale-spread inputs
+    run_case(synth.make(8192, H, seed=5, family=family, w_dtype="f32"), det=True, nsample=64)
+
+
+def test_nondet_spread_family():
+    run_case(synth.make(8192, 2048, seed=6, family="spread", w_dtype="f32"), det=False, nsample=64)
+
+
+# ---------------------------------------------------------------- edge cases --
+
+def test_zero_tokens():
+    x = torch.empty((0, 512), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones(512, dtype=torch.float32, device="cuda")
+    y, rstd = R.rmsnorm_train_fwd(x, w)
+    assert y.shape == (0, 512) and rstd.shape == (0,)
+    for det in (True, False):
+        dx, dw = R.rmsnorm_train_bwd(x, x, rstd, w, det)
+        torch.cuda.synchronize()
+        assert dx.shape == (0, 512)
+        assert torch.all(dw == 0)
+
+
+def test_zero_and_constant_rows():
+    # zero row: rstd = 1/sqrt(eps) = 1000, y = 0, dx = rstd * dy * w
+    T, H = 5, 1536
+    p = synth.make(T, H, seed=0, w_dtype="f32")
+    view = p.view(p.x)
+    view[0].zero_()
+    view[2].fill_(3.0)
+    out = run_case(p, det=True)
+    g = OnGpu(p)
+    _, rstd = R.rmsnorm_train_fwd(g.x, g.w)
+    assert abs(rstd[0].item() - 1000.0) <= 1000.0 * 1e-6
+    assert abs(rstd[2].item() - 1.0 / np.sqrt(9.0 + 1e-6)) <= 1e-6
+    assert out["dw"] <= 1.0
