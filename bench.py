@@ -75,8 +75,8 @@ def time_calls(fn, steps, warmup, torch):
     return ev, wall
 
 
-def cpu_baseline(p, rows_sample):
-    """The FP64 oracle (single-threaded C) on the first rows of the workload."""
+def cpu_baseline(p, rows_sample, reps=3):
+    """The FP64 oracle (single-threaded C) on the workload's rows: median of reps."""
     import numpy as np
     import torch
 
@@ -86,16 +86,46 @@ def cpu_baseline(p, rows_sample):
     xs = p.x.view(-1, W)[:rows_sample].contiguous().view(torch.int16).numpy().view(np.uint16)
     dys = p.dy.view(-1, W)[:rows_sample].contiguous().view(torch.int16).numpy().view(np.uint16)
     w64 = p.w.double().numpy()
-    t0 = time.perf_counter()
-    oracle.bwd(oracle.View.dense(dys), oracle.View.dense(xs), w64, p.eps)
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.bwd(oracle.View.dense(dys), oracle.View.dense(xs), w64, p.eps)
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[len(times) // 2]
     gbps = bwd_bytes(rows_sample, W, 4) / dt / 1e9
     return {
         "value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": f"backward (dx and dw) of the first {rows_sample} of {p.T} rows, width {W}, "
-                  f"{dt:.2f} s, same algorithmic byte model as value",
-        "us_per_call_scaled": round(dt * 1e6 * p.T / rows_sample, 1),
+        "sample": f"backward (dx for every row, dw over every row) of {rows_sample} of {p.T} "
+                  f"rows, width {W}, FP64 C oracle, median of {reps} runs ({dt:.2f} s each); "
+                  "same algorithmic byte model as value",
+        "us_per_call": round(dt * 1e6 * p.T / rows_sample, 1),
     }
+
+
+def traffic_probe():
+    """For rocprofv3 --pmc runs: one plain copy of known size (calibration),
+    then three backward calls at the headline shape."""
+    import torch
+
+    import rmsnorm_train_fwd_amd as R
+    from rmsnorm_train_fwd_amd import synth
+
+    dev = torch.device("cuda:0")
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)  # 1 GiB read + 1 GiB written
+    torch.cuda.synchronize()
+    del src, dst
+    p = synth.make(T_HEAD, H_HEAD, seed=0, w_dtype="f32")
+    x = p.x.to(dev).view(T_HEAD, H_HEAD)
+    dy = p.dy.to(dev).view(T_HEAD, H_HEAD)
+    w = p.w.to(dev)
+    _, rstd = R.rmsnorm_train_fwd(x, w, p.eps)
+    for _ in range(3):
+        R.rmsnorm_train_bwd(dy, x, rstd, w, False)
+    torch.cuda.synchronize()
+    print("[bench] traffic probe done", file=sys.stderr, flush=True)
 
 
 def main():
@@ -104,13 +134,19 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=16384)
+    ap.add_argument("--cpu-rows", type=int, default=T_HEAD)
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only run the copy + backward calls that the counter runs read")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by rows with one dw all-reduce; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.traffic_probe:
+        traffic_probe()
+        return
 
     import torch
 

@@ -111,7 +111,7 @@ void make_plan(const rmsn_layout& L, int /*det*/, const rmsn_launch* o, rmsn_bwd
   if (path == RMSN_PATH_AUTO)
     path = rows <= small_path_max_rows(L.width) ? RMSN_PATH_SMALL : RMSN_PATH_LARGE;
   p->path = path;
-  const int32_t col_tiles = (int32_t)(L.width / kColTile);
+  const int32_t col_tiles = (int32_t)(L.width / small_col_tile((int)L.width));
   if (path == RMSN_PATH_SMALL) {
     const int64_t tiles = cdiv(rows, p->subchains);
     p->grid = (o && o->grid) ? o->grid : (int32_t)(tiles < kMaxGrid ? tiles : kMaxGrid);
@@ -120,7 +120,7 @@ void make_plan(const rmsn_layout& L, int /*det*/, const rmsn_launch* o, rmsn_bwd
     p->workspace_bytes = 0;
   } else {
     p->grid = (o && o->grid) ? o->grid : (int32_t)p->chunks;
-    p->fold_grid = (o && o->fold_grid) ? o->fold_grid : col_tiles;
+    p->fold_grid = (o && o->fold_grid) ? o->fold_grid : (int32_t)(L.width / kFoldTile);
     p->workspace_bytes = (size_t)p->chunks * (size_t)L.width * sizeof(double);
   }
 }

@@ -4,25 +4,42 @@
 
 namespace rmsn {
 
-__global__ __launch_bounds__(kBlock) void k_fold(const double* __restrict__ ws,
-                                                 float* __restrict__ dw, int H, int64_t chunks) {
-  __shared__ double gsum[1024 / kFoldGroup][kColTile];
-  const int lane = threadIdx.x % kColTile, wave = threadIdx.x / kColTile;
-  constexpr int kWaves = kBlock / kColTile;
-  const int64_t groups = (chunks + kFoldGroup - 1) / kFoldGroup;  // <= 32 (chunks <= 1024)
-  for (int tile = blockIdx.x; tile < H / kColTile; tile += gridDim.x) {
-    const int col = tile * kColTile + lane;
-    for (int64_t g = wave; g < groups; g += kWaves) {
-      const int64_t k0 = g * kFoldGroup;
-      const int64_t k1 = k0 + kFoldGroup < chunks ? k0 + kFoldGroup : chunks;
+// One workgroup of kFoldThreads threads covers kFoldTile columns: thread
+// (g, c) sums group g of column c (its kFoldGroup chunk partials are loaded
+// first, then added in ascending order from 0.0), the group sums meet in LDS,
+// and one thread per column adds them in ascending group order from 0.0.
+// With one thread per (column, group) every partial of the call is in flight
+// at once.
+__global__ __launch_bounds__(kFoldThreads) void k_fold(const double* __restrict__ ws,
+                                                       float* __restrict__ dw, int H,
+                                                       int64_t chunks) {
+  constexpr int kGroups = kFoldThreads / kFoldTile;  // 32 = max groups (<= 1024 chunks)
+  __shared__ double gsum[kGroups][kFoldTile];
+  const int c = threadIdx.x % kFoldTile, g = threadIdx.x / kFoldTile;
+  const int64_t groups = (chunks + kFoldGroup - 1) / kFoldGroup;
+  for (int tile = blockIdx.x; tile < H / kFoldTile; tile += gridDim.x) {
+    const int col = tile * kFoldTile + c;
+    if (g < groups) {
+      const int64_t k0 = (int64_t)g * kFoldGroup;
+      const int n = (int)(chunks - k0 < kFoldGroup ? chunks - k0 : kFoldGroup);
+      const double* p = ws + k0 * H + col;
       double s = 0.0;
-      for (int64_t k = k0; k < k1; ++k) s = s + ws[k * H + col];
-      gsum[g][lane] = s;
+      constexpr int kBatch = 16;  // loads in flight per thread
+#pragma unroll
+      for (int i0 = 0; i0 < kFoldGroup; i0 += kBatch) {
+        double v[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) v[i] = i0 + i < n ? p[(int64_t)(i0 + i) * H] : 0.0;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+          if (i0 + i < n) s = s + v[i];
+      }
+      gsum[g][c] = s;
     }
     __syncthreads();
-    if (wave == 0) {
+    if (g == 0) {
       double t = 0.0;
-      for (int64_t g = 0; g < groups; ++g) t = t + gsum[g][lane];
+      for (int64_t gg = 0; gg < groups; ++gg) t = t + gsum[gg][c];
       dw[col] = (float)t;
     }
     __syncthreads();
@@ -30,12 +47,10 @@ __global__ __launch_bounds__(kBlock) void k_fold(const double* __restrict__ ws,
 }
 
 namespace {
-constexpr int kBwdD = 2;  // rows per row group per batch
-
 template <int H, bool WF32, int FORM>
 hipError_t large_mode(bool det, const BwdArgs& a, int grid, hipStream_t s) {
-  if (det) k_bwd_large<H, WF32, FORM, true, kBwdD><<<grid, kBlock, 0, s>>>(a);
-  else k_bwd_large<H, WF32, FORM, false, kBwdD><<<grid, kBlock, 0, s>>>(a);
+  if (det) k_bwd_large<H, WF32, FORM, true, Geo<H>::D><<<grid, Geo<H>::BLOCK, 0, s>>>(a);
+  else k_bwd_large<H, WF32, FORM, false, Geo<H>::D><<<grid, Geo<H>::BLOCK, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -71,7 +86,7 @@ hipError_t launch_bwd_large(int H, bool w_f32, int form, bool det, const BwdArgs
 }
 
 hipError_t launch_fold(int H, const BwdArgs& a, int grid, hipStream_t s) {
-  k_fold<<<grid, kBlock, 0, s>>>(a.ws, a.dw, H, a.chunks);
+  k_fold<<<grid, kFoldThreads, 0, s>>>(a.ws, a.dw, H, a.chunks);
   return hipGetLastError();
 }
 

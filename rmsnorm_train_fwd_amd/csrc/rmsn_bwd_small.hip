@@ -8,9 +8,9 @@ template <int H, bool WF32>
 hipError_t small_form(int form, const BwdArgs& a, int row_grid, int col_grid, hipStream_t s) {
   const int grid = row_grid + col_grid;
   switch (form) {
-    case kPlain: k_bwd_small<H, WF32, kPlain><<<grid, kBlock, 0, s>>>(a, row_grid); break;
-    case kResidual: k_bwd_small<H, WF32, kResidual><<<grid, kBlock, 0, s>>>(a, row_grid); break;
-    case kGate: k_bwd_small<H, WF32, kGate><<<grid, kBlock, 0, s>>>(a, row_grid); break;
+    case kPlain: k_bwd_small<H, WF32, kPlain><<<grid, Geo<H>::BLOCK, 0, s>>>(a, row_grid); break;
+    case kResidual: k_bwd_small<H, WF32, kResidual><<<grid, Geo<H>::BLOCK, 0, s>>>(a, row_grid); break;
+    case kGate: k_bwd_small<H, WF32, kGate><<<grid, Geo<H>::BLOCK, 0, s>>>(a, row_grid); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -21,6 +21,19 @@ hipError_t small_width(bool w_f32, int form, const BwdArgs& a, int rg, int cg, h
   return w_f32 ? small_form<H, true>(form, a, rg, cg, s) : small_form<H, false>(form, a, rg, cg, s);
 }
 }  // namespace
+
+int small_col_tile(int H) {
+  switch (H) {
+    case 256: return Geo<256>::BLOCK / kFoldGroup * 8;
+    case 512: return Geo<512>::BLOCK / kFoldGroup * 8;
+    case 1536: return Geo<1536>::BLOCK / kFoldGroup * 8;
+    case 2048: return Geo<2048>::BLOCK / kFoldGroup * 8;
+    case 4096: return Geo<4096>::BLOCK / kFoldGroup * 8;
+    case 5120: return Geo<5120>::BLOCK / kFoldGroup * 8;
+    case 6144: return Geo<6144>::BLOCK / kFoldGroup * 8;
+    default: return 0;
+  }
+}
 
 int bwd_rows_per_rowtask(int H) {
   switch (H) {

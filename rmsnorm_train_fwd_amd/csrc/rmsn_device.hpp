@@ -124,29 +124,45 @@ __device__ __forceinline__ float lane_sum(float v) {
 // A row of `H` BF16 elements is handled by a row group of TPR threads; each
 // thread owns V 16-byte vectors (8 elements each): vector v of lane l covers
 // elements (v*TPR + l)*8 .. +7, so one load instruction of the row group
-// reads TPR*16 contiguous bytes. A 256-thread workgroup holds R = 256/TPR
-// row groups, which work on R different rows at a time.
+// reads TPR*16 contiguous bytes. A workgroup of BLOCK = TPR*R threads holds R
+// row groups, which work on R different rows at a time; in the backward main
+// kernel each row group takes D rows per batch. The shapes keep each
+// thread at 8 columns: per-column state (weight, dw
+// accumulators) lives in registers, and fewer columns per thread means more
+// waves in flight.
 template <int H> struct Cfg;
-template <> struct Cfg<256>  { static constexpr int TPR = 32,  V = 1; };
-template <> struct Cfg<512>  { static constexpr int TPR = 64,  V = 1; };
-template <> struct Cfg<1536> { static constexpr int TPR = 64,  V = 3; };
-template <> struct Cfg<2048> { static constexpr int TPR = 128, V = 2; };
-template <> struct Cfg<4096> { static constexpr int TPR = 256, V = 2; };
-template <> struct Cfg<5120> { static constexpr int TPR = 128, V = 5; };
-template <> struct Cfg<6144> { static constexpr int TPR = 256, V = 3; };
-
-constexpr int kBlock = 256;
+template <> struct Cfg<256>  { static constexpr int TPR = 32,  V = 1, R = 16, D = 2; };
+template <> struct Cfg<512>  { static constexpr int TPR = 64,  V = 1, R = 8,  D = 2; };
+template <> struct Cfg<1536> { static constexpr int TPR = 192, V = 1, R = 4,  D = 2; };
+template <> struct Cfg<2048> { static constexpr int TPR = 256, V = 1, R = 4,  D = 1; };
+template <> struct Cfg<4096> { static constexpr int TPR = 512, V = 1, R = 2,  D = 1; };
+template <> struct Cfg<5120> { static constexpr int TPR = 640, V = 1, R = 1,  D = 1; };
+template <> struct Cfg<6144> { static constexpr int TPR = 768, V = 1, R = 1,  D = 1; };
 
 template <int H>
 struct Geo {
   static constexpr int TPR = Cfg<H>::TPR;
   static constexpr int V = Cfg<H>::V;
-  static constexpr int R = kBlock / TPR;           // row groups per workgroup
+  static constexpr int R = Cfg<H>::R;              // row groups per workgroup
+  static constexpr int BLOCK = TPR * R;            // workgroup size
   static constexpr int LANES = TPR < 64 ? TPR : 64;
   static constexpr int WPR = TPR / LANES;          // waves per row group
   static constexpr int E = 8 * V;                  // elements per thread
+  static constexpr int D = Cfg<H>::D;              // rows per row group per backward batch
   static_assert(TPR * V * 8 == H, "layout must tile the row exactly");
+  static_assert(TPR % 64 == 0 || TPR == 32, "row groups are half waves or whole waves");
+  static_assert(BLOCK <= 1024 && BLOCK % 32 == 0, "workgroup size");
 };
+
+// Row group of this thread. With whole-wave row groups it is the same for
+// every lane of a wave; saying so (readfirstlane) lets the compiler keep row
+// indices, row addresses and rstd in scalar registers.
+template <int H>
+__device__ __forceinline__ int row_group() {
+  const int q = threadIdx.x / Geo<H>::TPR;
+  if constexpr (Geo<H>::TPR >= 64) return __builtin_amdgcn_readfirstlane(q);
+  else return q;
+}
 
 // Weight in registers: the E elements a thread owns, as FP32.
 template <int H, bool WF32>

@@ -9,9 +9,9 @@ constexpr int kFwdRPG = 2;  // rows per row group per tile
 template <int H, bool WF32>
 hipError_t fwd_form(int form, const FwdArgs& a, int grid, hipStream_t s) {
   switch (form) {
-    case kPlain: k_fwd<H, WF32, kPlain, kFwdRPG><<<grid, kBlock, 0, s>>>(a); break;
-    case kResidual: k_fwd<H, WF32, kResidual, kFwdRPG><<<grid, kBlock, 0, s>>>(a); break;
-    case kGate: k_fwd<H, WF32, kGate, kFwdRPG><<<grid, kBlock, 0, s>>>(a); break;
+    case kPlain: k_fwd<H, WF32, kPlain, kFwdRPG><<<grid, Geo<H>::BLOCK, 0, s>>>(a); break;
+    case kResidual: k_fwd<H, WF32, kResidual, kFwdRPG><<<grid, Geo<H>::BLOCK, 0, s>>>(a); break;
+    case kGate: k_fwd<H, WF32, kGate, kFwdRPG><<<grid, Geo<H>::BLOCK, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -36,10 +36,10 @@ __device__ __forceinline__ int elem0(int v, int lane) {
 // differ by more than 16, and then the smaller one is far below half a BF16
 // ulp, so the result is the rounded exact sum), and the norm reads that h.
 template <int H, bool WF32, int FORM, int RPG>
-__global__ __launch_bounds__(kBlock) void k_fwd(FwdArgs a) {
+__global__ __launch_bounds__(Geo<H>::BLOCK) void k_fwd(FwdArgs a) {
   using G = Geo<H>;
   constexpr int R = G::R, V = G::V, E = G::E;
-  const int q = threadIdx.x / G::TPR, lane = threadIdx.x % G::TPR;
+  const int q = row_group<H>(), lane = threadIdx.x % G::TPR;
   __shared__ float slots[RowSum<H, RPG>::kSlots];
   int parity = 0;
   float wr[E];
@@ -117,6 +117,8 @@ __global__ __launch_bounds__(kBlock) void k_fwd(FwdArgs a) {
 // x, dy (and z) for the dw accumulation. The arithmetic of a row does not
 // depend on D or on the kernel calling it, so dx has the same bits on every
 // path.
+struct NoDw {};  // accumulator policy of row tasks that only write dx
+
 template <int H, int FORM, int D>
 struct RowBatch {
   static constexpr int V = Geo<H>::V, E = Geo<H>::E;
@@ -127,45 +129,97 @@ struct RowBatch {
                                        const bool (&ok)[D], int lane) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      const int64_t xo = ok[d] ? row_off(a.x, row[d], a.heads) : 0;
-      const int64_t go = ok[d] ? row_off(a.dy, row[d], a.heads) : 0;
-      const int64_t eo = ok[d] && FORM != kPlain ? row_off(a.e, row[d], a.heads) : 0;
-      r[d] = ok[d] ? a.rstd[row[d]] : 0.0f;
+      // Masked entries (ok[d] false) carry a valid row index chosen by the
+      // caller: they load real data, which is then ignored (no branches
+      // around the loads, so they issue back to back).
+      (void)ok;
+      const int64_t xo = row_off(a.x, row[d], a.heads);
+      const int64_t go = row_off(a.dy, row[d], a.heads);
+      const int64_t eo = FORM != kPlain ? row_off(a.e, row[d], a.heads) : 0;
+      r[d] = a.rstd[row[d]];
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         const int e0 = elem0<H>(v, lane);
-        xv[d][v] = ok[d] ? ld16_stream(a.x.p + xo + e0) : make_uint4(0, 0, 0, 0);
-        gv[d][v] = ok[d] ? ld16_stream(a.dy.p + go + e0) : make_uint4(0, 0, 0, 0);
-        if constexpr (FORM != kPlain)
-          ev[d][v] = ok[d] ? ld16_stream(a.e.p + eo + e0) : make_uint4(0, 0, 0, 0);
+        xv[d][v] = ld16_stream(a.x.p + xo + e0);
+        gv[d][v] = ld16_stream(a.dy.p + go + e0);
+        if constexpr (FORM != kPlain) ev[d][v] = ld16_stream(a.e.p + eo + e0);
       }
     }
   }
 
-  template <bool WF32>
+  // Make the loaded words look redefined to the compiler, so that values
+  // unpacked from them before this point are not kept live across it
+  // (re-unpacking is two VALU ops per element; keeping them live would cost
+  // 2-4 VGPRs per element and halve the waves in flight).
+  __device__ __forceinline__ void opaque() {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        asm volatile("" : "+v"(xv[d][v].x), "+v"(xv[d][v].y), "+v"(xv[d][v].z), "+v"(xv[d][v].w));
+        asm volatile("" : "+v"(gv[d][v].x), "+v"(gv[d][v].y), "+v"(gv[d][v].z), "+v"(gv[d][v].w));
+        if constexpr (FORM != kPlain)
+          asm volatile("" : "+v"(ev[d][v].x), "+v"(ev[d][v].y), "+v"(ev[d][v].z), "+v"(ev[d][v].w));
+      }
+    }
+  }
+
+  // Pass 1 (per row): the row sum c = sum g*xhat, and the row's dw terms into
+  // acc (they do not depend on c, so they are taken while x and dy are
+  // unpacked anyway). Row sum across the row group. Pass 2: dx (+dz), stores.
+  // Acc is Dot2 (deterministic: exact dy*x times rstd, or RN(rstd*silu) for
+  // the gate), Block8 (dy times xhat [* silu]) or NoDw (dx only).
+  template <bool WF32, class Acc>
   __device__ __forceinline__ void compute_store(const BwdArgs& a, const float (&wr)[E],
                                                 const int64_t (&row)[D], const bool (&ok)[D],
-                                                int q, int lane, float* slots, int& parity) {
+                                                int q, int lane, float* slots, int& parity,
+                                                Acc* acc) {
     float dot[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      float s = 0.0f;
+      float xf[E], gf[E], sl[E];
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        float xf[8], gf[8], zf[8];
-        unpack8(xv[d][v], xf);
-        unpack8(gv[d][v], gf);
-        if constexpr (FORM == kGate) unpack8(ev[d][v], zf);
+        float t[8];
+        unpack8(xv[d][v], t);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          float g = gf[k] * wr[v * 8 + k];
-          if constexpr (FORM == kGate) g = g * (zf[k] * sigmoid_f(zf[k]));
-          s = __builtin_fmaf(g, xf[k] * r[d], s);
+        for (int k = 0; k < 8; ++k) xf[v * 8 + k] = t[k];
+        unpack8(gv[d][v], t);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) gf[v * 8 + k] = t[k];
+        if constexpr (FORM == kGate) {
+          unpack8(ev[d][v], t);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) sl[v * 8 + k] = t[k] * sigmoid_f(t[k]);
         }
       }
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float g = gf[e] * wr[e];
+        if constexpr (FORM == kGate) g = g * sl[e];
+        s = __builtin_fmaf(g, xf[e] * r[d], s);
+      }
       dot[d] = s;
+      if constexpr (!__is_same(Acc, NoDw)) {
+        if (ok[d]) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            if constexpr (__is_same(Acc, Dot2)) {
+              float b = r[d];
+              if constexpr (FORM == kGate) b = r[d] * sl[e];
+              acc[e].add(gf[e] * xf[e], b);
+            } else {
+              float b = xf[e] * r[d];
+              if constexpr (FORM == kGate) b = b * sl[e];
+              acc[e].add(gf[e], b);
+            }
+          }
+        }
+      }
     }
     RowSum<H, D>::run(dot, slots, parity, q, lane);
+    opaque();
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const float c = dot[d] / (float)H;
@@ -188,43 +242,13 @@ struct RowBatch {
           if constexpr (FORM == kResidual) dx = zf[k] + dx;  // grad_h = dh + dx
           out[k] = dx;
         }
+        // Unconditional: a masked entry holds a copy of a real row of the
+        // same call (its index was clamped to that row), so it stores the very
+        // bytes that row's own pass stores; no branch around the stores.
         const int64_t o = row[d] * H + elem0<H>(v, lane);
-        if (ok[d]) {
-          st16_stream(a.dx + o, pack8(out));
-          if constexpr (FORM == kGate) st16_stream(a.dz + o, pack8(dz));
-        }
+        st16_stream(a.dx + o, pack8(out));
+        if constexpr (FORM == kGate) st16_stream(a.dz + o, pack8(dz));
       }
-    }
-  }
-
-  // dw terms of row d, element (v, k), into a deterministic accumulator:
-  // exact a = dy*x, times rstd (or RN(rstd*silu(z)) for the gate).
-  __device__ __forceinline__ void det_terms(int d, int v, float (&a8)[8], float (&b8)[8]) const {
-    float xf[8], gf[8];
-    unpack8(xv[d][v], xf);
-    unpack8(gv[d][v], gf);
-    float zf[8];
-    if constexpr (FORM == kGate) unpack8(ev[d][v], zf);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      a8[k] = gf[k] * xf[k];
-      b8[k] = r[d];
-      if constexpr (FORM == kGate) b8[k] = r[d] * (zf[k] * sigmoid_f(zf[k]));
-    }
-  }
-
-  // dw terms for the blocked FP32 accumulator: dy and xhat (* silu).
-  __device__ __forceinline__ void blk_terms(int d, int v, float (&a8)[8], float (&b8)[8]) const {
-    float xf[8], gf[8];
-    unpack8(xv[d][v], xf);
-    unpack8(gv[d][v], gf);
-    float zf[8];
-    if constexpr (FORM == kGate) unpack8(ev[d][v], zf);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      a8[k] = gf[k];
-      b8[k] = xf[k] * r[d];
-      if constexpr (FORM == kGate) b8[k] = b8[k] * (zf[k] * sigmoid_f(zf[k]));
     }
   }
 };
@@ -234,11 +258,11 @@ struct RowBatch {
 // D rows per batch, accumulating its sub-chain; the R sub-chains merge in
 // order through LDS in FP64 and the chunk partial goes to ws[k][:].
 template <int H, bool WF32, int FORM, bool DET, int D>
-__global__ __launch_bounds__(kBlock) void k_bwd_large(BwdArgs a) {
+__global__ __launch_bounds__(Geo<H>::BLOCK) void k_bwd_large(BwdArgs a) {
   using G = Geo<H>;
   constexpr int R = G::R, V = G::V, E = G::E, TPR = G::TPR;
   static_assert(8 % D == 0, "a batch must not straddle an 8-row block");
-  const int q = threadIdx.x / TPR, lane = threadIdx.x % TPR;
+  const int q = row_group<H>(), lane = threadIdx.x % TPR;
   __shared__ float slots[RowSum<H, D>::kSlots];
   __shared__ double merge[R > 1 ? H : 1];
   int parity = 0;
@@ -252,40 +276,55 @@ __global__ __launch_bounds__(kBlock) void k_bwd_large(BwdArgs a) {
     const int64_t r1 = r0 + C < a.rows ? r0 + C : a.rows;
     Dot2 dacc[DET ? E : 1];
     Block8 bacc[DET ? 1 : E];
-    for (int b = 0; b < nb; ++b) {
+    // Rows of batch b for this row group: k*C + (b*D + d)*R + q, d < D.
+    // Rows past the chunk end are masked and clamped to the chunk's first row.
+    auto rows_of = [&](int b, int64_t (&row)[D], bool (&ok)[D]) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const int64_t rr = r0 + (int64_t)(b * D + d) * R + q;
+        ok[d] = rr < r1;
+        row[d] = ok[d] ? rr : r0;
+      }
+    };
+    auto process = [&](RowBatch<H, FORM, D>& rb, int b) {
       int64_t row[D];
       bool ok[D];
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        row[d] = r0 + (int64_t)(b * D + d) * R + q;
-        ok[d] = row[d] < r1;
-      }
-      RowBatch<H, FORM, D> rb;
-      rb.load(a, row, ok, lane);
-      rb.template compute_store<WF32>(a, wr, row, ok, q, lane, slots, parity);
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        if (!ok[d]) continue;
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-          float a8[8], b8[8];
-          if constexpr (DET) {
-            rb.det_terms(d, v, a8, b8);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) dacc[v * 8 + i].add(a8[i], b8[i]);
-          } else {
-            rb.blk_terms(d, v, a8, b8);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) bacc[v * 8 + i].add(a8[i], b8[i]);
-          }
-        }
-      }
+      rows_of(b, row, ok);
+      if constexpr (DET) rb.template compute_store<WF32>(a, wr, row, ok, q, lane, slots, parity, dacc);
+      else rb.template compute_store<WF32>(a, wr, row, ok, q, lane, slots, parity, bacc);
       if constexpr (!DET) {
         if (((b + 1) * D) % 8 == 0) {
 #pragma unroll
           for (int e = 0; e < E; ++e) bacc[e].flush();
         }
       }
+    };
+    auto load = [&](RowBatch<H, FORM, D>& rb, int b) {
+      int64_t row[D];
+      bool ok[D];
+      rows_of(b, row, ok);
+      rb.load(a, row, ok, lane);
+    };
+    // Two batch buffers in turn: the loads of batch b+1 are in flight while
+    // batch b is reduced, written and accumulated. The steady-state loop
+    // issues its loads unconditionally (a load under a branch would make the
+    // compiler drain every outstanding load at the join); the last one or
+    // two batches are peeled.
+    RowBatch<H, FORM, D> ba, bb;
+    load(ba, 0);
+    int b = 0;
+    for (; b + 2 < nb; b += 2) {
+      load(bb, b + 1);
+      process(ba, b);
+      load(ba, b + 2);
+      process(bb, b + 1);
+    }
+    if (b + 1 < nb) {
+      load(bb, b + 1);
+      process(ba, b);
+      process(bb, b + 1);
+    } else {
+      process(ba, b);
     }
     double dv[E];
 #pragma unroll
@@ -320,56 +359,57 @@ __global__ __launch_bounds__(kBlock) void k_bwd_large(BwdArgs a) {
         }
         __syncthreads();
       }
-      for (int i = threadIdx.x; i < H; i += kBlock) out[i] = merge[i];
+      for (int i = threadIdx.x; i < H; i += Geo<H>::BLOCK) out[i] = merge[i];
       __syncthreads();
     }
   }
 }
 
 // Fold: dw[j] = RN_fp32( sum_g ( sum_{k in group g} ws[k][j] ) ), both sums in
-// ascending order from 0.0, groups of kFoldGroup consecutive chunks. One
-// workgroup covers kColTile columns: each wave sums whole groups, wave 0 adds
-// the group sums.
-__global__ __launch_bounds__(kBlock) void k_fold(const double* __restrict__ ws,
-                                                 float* __restrict__ dw, int H, int64_t chunks);
+// ascending order from 0.0, groups of kFoldGroup consecutive chunks (defined
+// in rmsn_bwd_large.hip).
+__global__ __launch_bounds__(kFoldThreads) void k_fold(const double* __restrict__ ws,
+                                                       float* __restrict__ dw, int H,
+                                                       int64_t chunks);
 
 // Small-row backward in one launch. Workgroups [0, row_grid) are row tasks
 // (dx, strided over row tiles of R rows); the rest are column tasks (dw),
-// strided over tiles of kColTile columns. A column-task thread (cv, kl) owns 8
+// strided over tiles of BLOCK/4 columns. A column-task thread (cv, kl) owns 8
 // columns and, per pass, chunk kl of the current fold group: it runs the R
 // sub-chains of its chunk exactly as k_bwd_large does, then the fold follows
 // k_fold's order through LDS. rstd is an input, so dw needs nothing from the
 // row tasks and no workgroup ever waits for another.
 template <int H, bool WF32, int FORM>
-__global__ __launch_bounds__(kBlock) void k_bwd_small(BwdArgs a, int row_grid) {
+__global__ __launch_bounds__(Geo<H>::BLOCK) void k_bwd_small(BwdArgs a, int row_grid) {
   using G = Geo<H>;
   constexpr int R = G::R, TPR = G::TPR;
   __shared__ float slots[RowSum<H, 1>::kSlots];
-  __shared__ double part[kFoldGroup][kColTile];
+  __shared__ double part[kFoldGroup][Geo<H>::BLOCK / kFoldGroup * 8];
   if ((int)blockIdx.x < row_grid) {
-    const int q = threadIdx.x / TPR, lane = threadIdx.x % TPR;
+    const int q = row_group<H>(), lane = threadIdx.x % TPR;
     int parity = 0;
     float wr[G::E];
     load_w<H, WF32>(a.w, lane, wr);
     const int64_t tiles = (a.rows + R - 1) / R;
     for (int64_t t = blockIdx.x; t < tiles; t += row_grid) {
-      int64_t row[1] = {t * R + q};
-      bool ok[1] = {row[0] < a.rows};
+      bool ok[1] = {t * R + q < a.rows};
+      int64_t row[1] = {ok[0] ? t * R + q : t * R};
       RowBatch<H, FORM, 1> rb;
       rb.load(a, row, ok, lane);
-      rb.template compute_store<WF32>(a, wr, row, ok, q, lane, slots, parity);
+      rb.template compute_store<WF32>(a, wr, row, ok, q, lane, slots, parity, (NoDw*)nullptr);
     }
     return;
   }
-  constexpr int CV = kColTile / 8;            // column vectors per tile
-  constexpr int KL = kBlock / CV;             // chunk lanes
-  static_assert(KL == kFoldGroup, "one pass of chunk lanes is one fold group");
+  constexpr int KL = kFoldGroup;              // chunk lanes: one pass = one fold group
+  constexpr int CV = G::BLOCK / KL;           // column vectors per tile
+  constexpr int kTile = CV * 8;               // columns per tile
+  static_assert(H % kTile == 0, "column tiles must cover the row exactly");
   const int cv = threadIdx.x % CV, kl = threadIdx.x / CV;
   const int col_grid = gridDim.x - row_grid;
   const int64_t C = a.chunk_rows;
   const int64_t groups = (a.chunks + kFoldGroup - 1) / kFoldGroup;
-  for (int tile = blockIdx.x - row_grid; tile < H / kColTile; tile += col_grid) {
-    const int c0 = tile * kColTile + cv * 8;
+  for (int tile = blockIdx.x - row_grid; tile < H / kTile; tile += col_grid) {
+    const int c0 = tile * kTile + cv * 8;
     double total[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) total[i] = 0.0;

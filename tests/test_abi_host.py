@@ -192,11 +192,11 @@ def test_canonical_chunking(rows):
 
 def test_plan_headline_and_paths():
     p = query(131072, 4096)
-    assert (p.chunk_rows, p.chunks, p.subchains, p.fold_group) == (128, 1024, 1, 32)
-    assert p.workspace_bytes == 1024 * 4096 * 8 and p.grid == 1024 and p.fold_grid == 64
+    assert (p.chunk_rows, p.chunks, p.subchains, p.fold_group) == (128, 1024, 2, 32)
+    assert p.workspace_bytes == 1024 * 4096 * 8 and p.grid == 1024 and p.fold_grid == 128
     s = query(8, 512)
-    assert s.path == R.PATH_SMALL and s.workspace_bytes == 0 and s.subchains == 4
-    assert query(4, 256, heads=24).subchains == 8
+    assert s.path == R.PATH_SMALL and s.workspace_bytes == 0 and s.subchains == 8
+    assert query(4, 256, heads=24).subchains == 16
     z = query(0, 6144)
     assert z.path == R.PATH_SMALL and z.grid == 0 and z.workspace_bytes == 0
     forced = query(100, 2048, launch=R.Launch(0, 0, R.PATH_LARGE))
