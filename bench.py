@@ -128,6 +128,311 @@ def traffic_probe():
     print("[bench] traffic probe done", file=sys.stderr, flush=True)
 
 
+def sweep(out_path, reps=20):
+    """Every workload of the build, one graph-replayed call per timing with a
+    512 MB write between calls (cold L2 and Infinity Cache). Writes a markdown
+    table to out_path and returns the rows."""
+    import torch
+
+    import rmsnorm_train_fwd_amd as R
+    from rmsnorm_train_fwd_amd import synth
+
+    dev = torch.device("cuda:0")
+    # Cold caches: read (not write) 512 MB between calls, evicting L2 and the
+    # 256 MB Infinity Cache without leaving dirty lines whose write-back would
+    # land inside the timed call.
+    flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
+
+    def graph_time(fn):
+        fn()  # allocations (outputs, workspace) happen outside capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        ts = []
+        # a marker range per case lets a rocprofv3 --marker-trace run attribute
+        # the kernels of these replays to this case (bench.py --sweep-kernels)
+        torch.cuda.nvtx.range_push(f"rmsn_case_{len(rows)}")
+        for _ in range(reps):
+            flush.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        torch.cuda.nvtx.range_pop()
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    rows = []
+
+    def add(cfg, shape, op, us, nbytes):
+        gbps = nbytes / (us * 1e-6) / 1e9 if nbytes else None
+        rows.append((cfg, shape, op, us, gbps))
+        pct = f"{100 * gbps / HBM_PEAK_GBPS:.1f}%" if gbps else "-"
+        print(f"[sweep] {cfg:4s} {shape:34s} {op:26s} {us:9.2f} us  "
+              f"{(f'{gbps:7.0f} GB/s' if gbps else ''):>12s} {pct}", file=sys.stderr, flush=True)
+
+    def run_plain(cfg, T, H, w_dtype, modes, heads=1, rs=None, hs=None, fwd=True, label=None):
+        p = synth.make(T, H, seed=0, heads=heads, w_dtype=w_dtype, row_stride=rs, head_stride=hs)
+        wb = 4 if w_dtype == "f32" else 2
+        x = p.x.to(dev).as_strided(*((p.T, p.width), (p.row_stride, 1)) if heads == 1 else
+                                    ((p.T, heads, p.width), (p.row_stride, p.head_stride, 1)))
+        dy = p.dy.to(dev).as_strided(x.shape, x.stride())
+        w = p.w.to(dev)
+        y, rstd = R.rmsnorm_train_fwd(x, w, p.eps)
+        rws = p.rows
+        shape = label or f"[{T},{H}] w {w_dtype}"
+        if fwd:
+            add(cfg, shape, "fwd", graph_time(lambda: R.rmsnorm_train_fwd(x, w, p.eps)),
+                fwd_bytes(rws, H, wb))
+        for det in modes:
+            plan = R.rmsnorm_train_bwd_query(x, det, dy=dy)
+            ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+            path = "small" if plan.path == R.PATH_SMALL else "large"
+            add(cfg, shape, f"bwd {'det' if det else 'nondet'} ({path})",
+                graph_time(lambda: R.rmsnorm_train_bwd(dy, x, rstd, w, det, workspace=ws)),
+                bwd_bytes(rws, H, wb))
+
+    tiny = torch.zeros(1, device=dev)
+    add("-", "launch floor: 1-element kernel", "graph replay", graph_time(lambda: tiny.add_(1)), 0)
+    run_plain("1", 8, 512, "bf16", [True], label="[8,512] w bf16")
+    for H in (512, 1536, 2048, 4096, 5120, 6144):
+        for T in (1, 8, 32, 128, 203):
+            for wd in ("f32", "bf16"):
+                run_plain("2", T, H, wd, [True], fwd=False)
+    for T in (1, 32, 203):
+        for (rs, hs) in ((12288, 512), (6144, 256)):
+            run_plain("2", T, 256, "f32", [True], heads=24, rs=rs, hs=hs, fwd=False,
+                      label=f"[{T},24,256] strides ({rs},{hs},1)")
+    for H in (1536, 2048, 4096, 5120, 6144):
+        for T in (65537, 98304, 131072):
+            run_plain("3", T, H, "f32", [False, True])
+            torch.cuda.empty_cache()
+    # fused residual, width 6144
+    for T in (32, 65537, 131072):
+        for wd in ("bf16", "f32"):
+            p = synth.make(T, 6144, seed=0, w_dtype=wd, form="residual")
+            wb = 4 if wd == "f32" else 2
+            x, res = p.x.to(dev).view(T, 6144), p.extra.to(dev).view(T, 6144)
+            dy, dh = p.dy.to(dev).view(T, 6144), p.dh.to(dev).view(T, 6144)
+            w = p.w.to(dev)
+            y, rstd, h = R.rmsnorm_train_fwd(x, w, p.eps, residual=res)
+            shape = f"[{T},6144] residual w {wd}"
+            add("4", shape, "fwd", graph_time(lambda: R.rmsnorm_train_fwd(x, w, p.eps, residual=res)),
+                8 * T * 6144 + 4 * T + wb * 6144)
+            for det in (False, True):
+                plan = R.rmsnorm_train_bwd_query(h, det)
+                ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+                add("4", shape, f"bwd {'det' if det else 'nondet'}",
+                    graph_time(lambda: R.rmsnorm_train_bwd(dy, h, rstd, w, det, dh=dh, workspace=ws)),
+                    8 * T * 6144 + 4 * T + wb * 6144 + 4 * 6144)
+            del x, res, dy, dh, y, h
+            torch.cuda.empty_cache()
+    # SiLU gate, width 4096: fwd, bwd, checkpointed step (fwd, fwd recompute, bwd)
+    for T in (3534, 8192, 16384):
+        p = synth.make(T, 4096, seed=0, w_dtype="f32", form="gate")
+        x, z = p.x.to(dev).view(T, 4096), p.extra.to(dev).view(T, 4096)
+        dy = p.dy.to(dev).view(T, 4096)
+        w = p.w.to(dev)
+        y, rstd = R.rmsnorm_silu_gate_train_fwd(x, z, w, p.eps)
+        shape = f"[{T},4096] gate w f32"
+        fb, bb = 6 * T * 4096 + 4 * T + 4 * 4096, 10 * T * 4096 + 4 * T + 8 * 4096
+        add("5", shape, "fwd", graph_time(lambda: R.rmsnorm_silu_gate_train_fwd(x, z, w, p.eps)), fb)
+        for det in (False, True):
+            plan = R.rmsnorm_train_bwd_query(x, det)
+            ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+            add("5", shape, f"bwd {'det' if det else 'nondet'}", graph_time(
+                lambda: R.rmsnorm_silu_gate_train_bwd(dy, x, z, rstd, w, det, workspace=ws)), bb)
+
+            def step():
+                R.rmsnorm_silu_gate_train_fwd(x, z, w, p.eps)
+                _, r2 = R.rmsnorm_silu_gate_train_fwd(x, z, w, p.eps)
+                R.rmsnorm_silu_gate_train_bwd(dy, x, z, r2, w, det, workspace=ws)
+            add("5", shape, f"step 2xfwd+bwd {'det' if det else 'nondet'}", graph_time(step),
+                2 * fb + bb)
+    with open(out_path, "w") as fh:
+        fh.write("| cfg | workload | op | us/call | algorithmic GB/s | % of 8 TB/s |\n|---|---|---|---|---|---|\n")
+        for cfg, shape, op, us, gbps in rows:
+            fh.write(f"| {cfg} | {shape} | {op} | {us:.2f} | {f'{gbps:.0f}' if gbps else '-'} | "
+                     f"{f'{100 * gbps / HBM_PEAK_GBPS:.1f}' if gbps else '-'} |\n")
+    with open(out_path + ".json", "w") as fh:
+        json.dump([{"case": i, "cfg": c, "workload": sh, "op": op, "event_us": us,
+                    "bytes": (None if g is None else g * us * 1e3)}
+                   for i, (c, sh, op, us, g) in enumerate(rows)], fh)
+    return rows
+
+
+def sweep_kernels(sweep_json, trace_dir, out_md):
+    """Kernel-active span per call from a rocprofv3 --kernel-trace --marker-trace
+    run of --sweep: per marker range (one case), the dispatches of this
+    library between two cache-flush dispatches form one replay; its span runs
+    from the first start to the last end. Median over the replays."""
+    import csv
+    import glob
+
+    cases = json.load(open(sweep_json))
+    kt = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    mt = glob.glob(os.path.join(trace_dir, "**", "*marker_api_trace.csv"), recursive=True)
+    if not kt or not mt:
+        raise SystemExit(f"no kernel/marker trace under {trace_dir}")
+    kern = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"])
+                   for r in csv.DictReader(open(kt[0]))))
+    ranges = {}
+    for r in csv.DictReader(open(mt[0])):
+        msg = r.get("Message") or r.get("Function") or ""
+        if msg.startswith("rmsn_case_"):
+            ranges[int(msg.split("_")[-1])] = (int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+    out = ["# Every workload: kernel-active time per call, cold caches (rocprofv3)", "",
+           "Commands (repository root $REPO on the MI355X box; committed files only):", "", "```",
+           "cd /tmp && export TMPDIR=/tmp",
+           "rocprofv3 --kernel-trace --marker-trace --output-format csv -d $REPO/gpurun_out/prof_sweep "
+           "-o sweep -- python3 $REPO/bench.py --sweep $REPO/gpurun_out/sweep.md",
+           "python3 $REPO/bench.py --sweep-kernels $REPO/gpurun_out/sweep.md.json "
+           "$REPO/gpurun_out/prof_sweep <this file>", "```", "",
+           "Each call is one graph replay after a 512 MB read that evicts L2 and the Infinity Cache. "
+           "Kernel-active span = first kernel start to last kernel end of the call (all of this "
+           "library's kernels of the call: main + fold on the large path), median of 20 calls. "
+           "The event column is the HIP-event time around the replay, which carries a ~13 us "
+           "floor on this system (a one-element kernel measures 13.4 us that way). GB/s uses the "
+           "algorithmic bytes: fwd 4TH, bwd 6TH, residual 8TH each way, gate fwd 6TH and bwd "
+           "10TH (+ per-row and per-column terms).", "",
+           "| cfg | workload | op | kernel-active us/call | algorithmic GB/s | % of 8 TB/s | event us/call |",
+           "|---|---|---|---|---|---|---|"]
+    for c in cases:
+        if c["case"] not in ranges or c["cfg"] == "-":
+            continue
+        t0, t1 = ranges[c["case"]]
+        spans, cur = [], None
+        for s_, e_, name in kern:
+            if s_ < t0 or s_ > t1:
+                continue
+            ours = "rmsn::" in name or c["cfg"] == "-"
+            flush = not ours or ("reduce" in name and c["cfg"] == "-")
+            if flush:
+                if cur:
+                    spans.append(cur[1] - cur[0])
+                cur = None
+            else:
+                cur = (s_, e_) if cur is None else (cur[0], max(cur[1], e_))
+        if cur:
+            spans.append(cur[1] - cur[0])
+        if not spans:
+            continue
+        spans.sort()
+        us = spans[len(spans) // 2] / 1e3
+        gbps = c["bytes"] / (us * 1e3) if c["bytes"] else None
+        out.append(f"| {c['cfg']} | {c['workload']} | {c['op']} | {us:.2f} | "
+                   f"{f'{gbps:.0f}' if gbps else '-'} | "
+                   f"{f'{100 * gbps / HBM_PEAK_GBPS:.1f}' if gbps else '-'} | {c['event_us']:.2f} |")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+def stats_report(stats_csv, out_md, command):
+    """Markdown table of a rocprofv3 --stats kernel summary, with algorithmic
+    GB/s for the headline kernels."""
+    import csv
+
+    lines = ["# rocprofv3 kernel statistics: backward and forward at [131072, 4096] BF16 (w FP32)",
+             "", "Command (repository root $REPO on the MI355X box; committed files only):", "",
+             "```", "cd /tmp && export TMPDIR=/tmp", command,
+             f"python3 $REPO/bench.py --stats-report <run_kernel_stats.csv> <this file>", "```", "",
+             f"Algorithmic bytes: backward call {bwd_bytes(T_HEAD, H_HEAD, 4):,} B; forward "
+             f"{fwd_bytes(T_HEAD, H_HEAD, 4):,} B.", "",
+             "| kernel | calls | avg us | min us | max us | algorithmic GB/s (avg) |",
+             "|---|---|---|---|---|---|"]
+    for r in csv.DictReader(open(stats_csv)):
+        n = r["Name"].strip('"')
+        avg = float(r["AverageNs"]) / 1e3
+        gb = ""
+        if "k_bwd_large" in n:
+            gb = f"{bwd_bytes(T_HEAD, H_HEAD, 4) / (avg * 1e-6) / 1e9:.0f} (main kernel alone)"
+        elif "k_fwd" in n:
+            gb = f"{fwd_bytes(T_HEAD, H_HEAD, 4) / (avg * 1e-6) / 1e9:.0f}"
+        lines.append(f"| `{n}` | {r['Calls']} | {avg:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {gb} |")
+    lines += ["", "k_bwd_large template arguments: <width, FP32 weight, form (0 = plain), "
+              "deterministic, rows per batch>. One backward call = k_bwd_large + k_fold."]
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def traffic_report(fetch_dir, write_dir, out_json, out_md):
+    """Calibrated HBM bytes per backward call from two rocprofv3 --pmc runs of
+    --traffic-probe (FETCH_SIZE, then WRITE_SIZE), scaled by the readings for
+    the 1 GiB device-to-device copy of known size."""
+    import csv
+    import glob
+
+    def load(d):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        return list(csv.DictReader(open(f)))
+
+    F, W = load(fetch_dir), load(write_dir)
+    GiB = 1 << 30
+
+    def copy_kib(rows):
+        v = [float(r["Counter_Value"]) for r in rows
+             if "copyBuffer" in r["Kernel_Name"] and r["Grid_Size"] == str(GiB // 8192)]
+        return v[0]
+
+    ff, wf = GiB / (copy_kib(F) * 1024), GiB / (copy_kib(W) * 1024)
+
+    def per(rows, key, factor):
+        v = [float(r["Counter_Value"]) * 1024 * factor for r in rows if key in r["Kernel_Name"]]
+        return sum(v) / len(v)
+
+    kr, kw = per(F, "k_bwd_large", ff), per(W, "k_bwd_large", wf)
+    fr, fw = per(F, "k_fold", ff), per(W, "k_fold", wf)
+    total, alg = kr + kw + fr + fw, bwd_bytes(T_HEAD, H_HEAD, 4)
+    out = {"kernel_hash": kernel_hash(),
+           "workload": "rmsnorm_train_bwd non-deterministic [131072,4096] BF16, w FP32",
+           "bytes_per_call": round(total), "algorithmic_bytes_per_call": alg,
+           "ratio_to_algorithmic": round(total / alg, 5), "fetch_scale": round(ff, 6),
+           "write_scale": round(wf, 6), "k_bwd_large": {"read": round(kr), "write": round(kw)},
+           "k_fold": {"read": round(fr), "write": round(fw)},
+           "calibration_kib": {"fetch": copy_kib(F), "write": copy_kib(W)}}
+    with open(out_json, "w") as fh:
+        json.dump(out, fh, indent=1)
+    md = f"""# HBM traffic of the backward call at [131072, 4096] (rocprofv3 counters)
+
+Commands (repository root $REPO on the MI355X box; committed files only; one counter per run):
+
+```
+cd /tmp && export TMPDIR=/tmp
+timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch -o run -- python3 $REPO/bench.py --traffic-probe
+timeout -s KILL 240 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write -o run -- python3 $REPO/bench.py --traffic-probe
+python3 $REPO/bench.py --traffic-report $REPO/gpurun_out/pmc_fetch $REPO/gpurun_out/pmc_write <json> <this file>
+```
+
+`bench.py --traffic-probe` runs one 1 GiB device-to-device copy (torch `copy_`, dispatched as
+`__amd_rocclr_copyBuffer`), the forward once and the non-deterministic backward three times.
+Calibration with that copy of known size (1 GiB read, 1 GiB written): FETCH_SIZE read
+{copy_kib(F):.1f} KiB and WRITE_SIZE {copy_kib(W):.1f} KiB, so read bytes = FETCH_SIZE x 1024 x
+{ff:.5f} and written bytes = WRITE_SIZE x 1024 x {wf:.5f}.
+
+| kernel (per dispatch, mean of 3) | read (scaled) | written (scaled) |
+|---|---|---|
+| k_bwd_large<4096, w FP32, plain, non-det> | {kr / 1e9:.4f} GB | {kw / 1e9:.4f} GB |
+| k_fold | {fr / 1e9:.4f} GB | {fw / 1e6:.3f} MB |
+| **backward call** | **{(kr + fr) / 1e9:.4f} GB** | **{(kw + fw) / 1e9:.4f} GB** |
+
+Algorithmic: reads x, dy, rstd, w = {(4 * T_HEAD * H_HEAD + 4 * T_HEAD + 4 * H_HEAD) / 1e9:.4f} GB;
+writes dx, dw = {(2 * T_HEAD * H_HEAD + 4 * H_HEAD) / 1e9:.4f} GB; total {alg / 1e9:.4f} GB.
+Measured {total / 1e9:.4f} GB per call, {100 * (total / alg - 1):.2f}% above it: the FP64 chunk
+partials (1024 x 4096 x 8 B = 32 MiB) written by the main kernel and read back by the fold.
+x, dy and dx are each moved once. Kernel sources hash: {out['kernel_hash']} (bench.py reports
+`traffic` only while the current sources hash to this value).
+"""
+    with open(out_md, "w") as fh:
+        fh.write(md)
+    print(md)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,7 +442,25 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=T_HEAD)
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run the copy + backward calls that the counter runs read")
+    ap.add_argument("--sweep", metavar="OUT.md",
+                    help="time every workload (cold caches, graph replay) into a markdown table")
+    ap.add_argument("--sweep-kernels", nargs=3, metavar=("SWEEP.md.json", "TRACE_DIR", "OUT.md"),
+                    help="kernel-active times of a --sweep run traced by rocprofv3")
+    ap.add_argument("--stats-report", nargs=2, metavar=("KERNEL_STATS.csv", "OUT.md"))
+    ap.add_argument("--traffic-report", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "OUT.json", "OUT.md"))
     args = ap.parse_args()
+    if args.stats_report:
+        stats_report(*args.stats_report,
+                     "rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/prof_bench "
+                     "-o run -- python3 $REPO/bench.py --steps 20 --warmup 5 --no-cpu")
+        return
+    if args.traffic_report:
+        traffic_report(*args.traffic_report)
+        return
+    if args.sweep_kernels:
+        sweep_kernels(*args.sweep_kernels)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by rows with one dw all-reduce; see the design notes)",
@@ -146,6 +469,9 @@ def main():
 
     if args.traffic_probe:
         traffic_probe()
+        return
+    if args.sweep:
+        sweep(args.sweep)
         return
 
     import torch

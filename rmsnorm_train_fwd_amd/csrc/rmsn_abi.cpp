@@ -17,7 +17,7 @@ using namespace rmsn;
 constexpr int64_t kWidths[] = {256, 512, 1536, 2048, 4096, 5120, 6144};
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxChunks = 1024;     // chunk partials per call (workspace bound)
-constexpr int64_t kChunkQuantum = 16;    // chunk rows are a multiple of this
+constexpr int64_t kMinChunkRows = 16;    // smallest chunk
 constexpr int64_t kMaxStride = int64_t(1) << 40;
 constexpr int32_t kMaxGrid = 1 << 24;
 
@@ -99,9 +99,11 @@ void make_plan(const rmsn_layout& L, int /*det*/, const rmsn_launch* o, rmsn_bwd
   memset(p, 0, sizeof *p);
   const int64_t rows = L.T * L.heads;
   p->rows = rows;
-  // Canonical chunking of the dw tree: depends on the row count only.
-  int64_t c = cdiv(cdiv(rows, kMaxChunks), kChunkQuantum) * kChunkQuantum;
-  if (c < kChunkQuantum) c = kChunkQuantum;
+  // Canonical chunking of the dw tree: depends on the row count only. The
+  // smallest C >= 16 with at most 1024 chunks, so large calls always have
+  // close to 1024 equal chunks (whole rounds of resident workgroups).
+  int64_t c = cdiv(rows, kMaxChunks);
+  if (c < kMinChunkRows) c = kMinChunkRows;
   p->chunk_rows = c;
   p->chunks = cdiv(rows, c);
   p->subchains = rows_per_subchain_group(L.width);
@@ -113,7 +115,7 @@ void make_plan(const rmsn_layout& L, int /*det*/, const rmsn_launch* o, rmsn_bwd
   p->path = path;
   const int32_t col_tiles = (int32_t)(L.width / small_col_tile((int)L.width));
   if (path == RMSN_PATH_SMALL) {
-    const int64_t tiles = cdiv(rows, p->subchains);
+    const int64_t tiles = cdiv(rows, small_rows_per_rowtask((int)L.width));
     p->grid = (o && o->grid) ? o->grid : (int32_t)(tiles < kMaxGrid ? tiles : kMaxGrid);
     if (rows == 0) p->grid = 0;
     p->fold_grid = (o && o->fold_grid) ? o->fold_grid : col_tiles;

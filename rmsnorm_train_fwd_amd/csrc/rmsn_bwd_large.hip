@@ -49,8 +49,8 @@ __global__ __launch_bounds__(kFoldThreads) void k_fold(const double* __restrict_
 namespace {
 template <int H, bool WF32, int FORM>
 hipError_t large_mode(bool det, const BwdArgs& a, int grid, hipStream_t s) {
-  if (det) k_bwd_large<H, WF32, FORM, true, Geo<H>::D><<<grid, Geo<H>::BLOCK, 0, s>>>(a);
-  else k_bwd_large<H, WF32, FORM, false, Geo<H>::D><<<grid, Geo<H>::BLOCK, 0, s>>>(a);
+  if (det) k_bwd_large<H, WF32, FORM, true, BwdShape<H, FORM>::D><<<grid, Geo<H>::BLOCK, 0, s>>>(a);
+  else k_bwd_large<H, WF32, FORM, false, BwdShape<H, FORM>::D><<<grid, Geo<H>::BLOCK, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -8,9 +8,9 @@ template <int H, bool WF32>
 hipError_t small_form(int form, const BwdArgs& a, int row_grid, int col_grid, hipStream_t s) {
   const int grid = row_grid + col_grid;
   switch (form) {
-    case kPlain: k_bwd_small<H, WF32, kPlain><<<grid, Geo<H>::BLOCK, 0, s>>>(a, row_grid); break;
-    case kResidual: k_bwd_small<H, WF32, kResidual><<<grid, Geo<H>::BLOCK, 0, s>>>(a, row_grid); break;
-    case kGate: k_bwd_small<H, WF32, kGate><<<grid, Geo<H>::BLOCK, 0, s>>>(a, row_grid); break;
+    case kPlain: k_bwd_small<H, WF32, kPlain><<<grid, SmallGeo<H>::BLOCK, 0, s>>>(a, row_grid); break;
+    case kResidual: k_bwd_small<H, WF32, kResidual><<<grid, SmallGeo<H>::BLOCK, 0, s>>>(a, row_grid); break;
+    case kGate: k_bwd_small<H, WF32, kGate><<<grid, SmallGeo<H>::BLOCK, 0, s>>>(a, row_grid); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -24,13 +24,26 @@ hipError_t small_width(bool w_f32, int form, const BwdArgs& a, int rg, int cg, h
 
 int small_col_tile(int H) {
   switch (H) {
-    case 256: return Geo<256>::BLOCK / kFoldGroup * 8;
-    case 512: return Geo<512>::BLOCK / kFoldGroup * 8;
-    case 1536: return Geo<1536>::BLOCK / kFoldGroup * 8;
-    case 2048: return Geo<2048>::BLOCK / kFoldGroup * 8;
-    case 4096: return Geo<4096>::BLOCK / kFoldGroup * 8;
-    case 5120: return Geo<5120>::BLOCK / kFoldGroup * 8;
-    case 6144: return Geo<6144>::BLOCK / kFoldGroup * 8;
+    case 256: return SmallGeo<256>::BLOCK / (kFoldGroup * Geo<256>::R) * 8;
+    case 512: return SmallGeo<512>::BLOCK / (kFoldGroup * Geo<512>::R) * 8;
+    case 1536: return SmallGeo<1536>::BLOCK / (kFoldGroup * Geo<1536>::R) * 8;
+    case 2048: return SmallGeo<2048>::BLOCK / (kFoldGroup * Geo<2048>::R) * 8;
+    case 4096: return SmallGeo<4096>::BLOCK / (kFoldGroup * Geo<4096>::R) * 8;
+    case 5120: return SmallGeo<5120>::BLOCK / (kFoldGroup * Geo<5120>::R) * 8;
+    case 6144: return SmallGeo<6144>::BLOCK / (kFoldGroup * Geo<6144>::R) * 8;
+    default: return 0;
+  }
+}
+
+int small_rows_per_rowtask(int H) {
+  switch (H) {
+    case 256: return SmallGeo<256>::RS;
+    case 512: return SmallGeo<512>::RS;
+    case 1536: return SmallGeo<1536>::RS;
+    case 2048: return SmallGeo<2048>::RS;
+    case 4096: return SmallGeo<4096>::RS;
+    case 5120: return SmallGeo<5120>::RS;
+    case 6144: return SmallGeo<6144>::RS;
     default: return 0;
   }
 }

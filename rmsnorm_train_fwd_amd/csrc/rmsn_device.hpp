@@ -126,18 +126,19 @@ __device__ __forceinline__ float lane_sum(float v) {
 // elements (v*TPR + l)*8 .. +7, so one load instruction of the row group
 // reads TPR*16 contiguous bytes. A workgroup of BLOCK = TPR*R threads holds R
 // row groups, which work on R different rows at a time; in the backward main
-// kernel each row group takes D rows per batch. The shapes keep each
+// kernel each row group takes D rows per batch, with the next batch's loads in
+// flight during the current one (PIPE) or not. The shapes keep each
 // thread at 8 columns: per-column state (weight, dw
 // accumulators) lives in registers, and fewer columns per thread means more
 // waves in flight.
 template <int H> struct Cfg;
-template <> struct Cfg<256>  { static constexpr int TPR = 32,  V = 1, R = 16, D = 2; };
-template <> struct Cfg<512>  { static constexpr int TPR = 64,  V = 1, R = 8,  D = 2; };
-template <> struct Cfg<1536> { static constexpr int TPR = 192, V = 1, R = 4,  D = 2; };
-template <> struct Cfg<2048> { static constexpr int TPR = 256, V = 1, R = 4,  D = 1; };
-template <> struct Cfg<4096> { static constexpr int TPR = 512, V = 1, R = 2,  D = 1; };
-template <> struct Cfg<5120> { static constexpr int TPR = 640, V = 1, R = 1,  D = 1; };
-template <> struct Cfg<6144> { static constexpr int TPR = 768, V = 1, R = 1,  D = 1; };
+template <> struct Cfg<256>  { static constexpr int TPR = 32,  V = 1, R = 16, D = 2; static constexpr bool PIPE = true; };
+template <> struct Cfg<512>  { static constexpr int TPR = 64,  V = 1, R = 8,  D = 4; static constexpr bool PIPE = false; };
+template <> struct Cfg<1536> { static constexpr int TPR = 192, V = 1, R = 4,  D = 4; static constexpr bool PIPE = false; };
+template <> struct Cfg<2048> { static constexpr int TPR = 256, V = 1, R = 4,  D = 1; static constexpr bool PIPE = true; };
+template <> struct Cfg<4096> { static constexpr int TPR = 512, V = 1, R = 2,  D = 1; static constexpr bool PIPE = true; };
+template <> struct Cfg<5120> { static constexpr int TPR = 640, V = 1, R = 1,  D = 1; static constexpr bool PIPE = true; };
+template <> struct Cfg<6144> { static constexpr int TPR = 768, V = 1, R = 1,  D = 4; static constexpr bool PIPE = false; };
 
 template <int H>
 struct Geo {
@@ -149,6 +150,7 @@ struct Geo {
   static constexpr int WPR = TPR / LANES;          // waves per row group
   static constexpr int E = 8 * V;                  // elements per thread
   static constexpr int D = Cfg<H>::D;              // rows per row group per backward batch
+  static constexpr bool PIPE = Cfg<H>::PIPE;       // backward: next batch loads during this one
   static_assert(TPR * V * 8 == H, "layout must tile the row exactly");
   static_assert(TPR % 64 == 0 || TPR == 32, "row groups are half waves or whole waves");
   static_assert(BLOCK <= 1024 && BLOCK % 32 == 0, "workgroup size");

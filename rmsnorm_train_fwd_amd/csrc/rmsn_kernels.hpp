@@ -253,6 +253,17 @@ struct RowBatch {
   }
 };
 
+// Batch shape of the backward main kernel for one form: the width's default,
+// except that the gated form (which also carries z) keeps to one row per
+// batch, pipelined, where the default is a multi-row burst (the burst would
+// not fit in registers).
+template <int H, int FORM>
+struct BwdShape {
+  static constexpr bool kGateBurst = FORM == kGate && !Geo<H>::PIPE;
+  static constexpr int D = kGateBurst ? 1 : Geo<H>::D;
+  static constexpr bool PIPE = kGateBurst ? true : Geo<H>::PIPE;
+};
+
 // Backward main kernel. Workgroup-strided over the canonical chunks of the dw
 // tree; inside a chunk, row group q walks rows k*C + q + i*R in ascending i,
 // D rows per batch, accumulating its sub-chain; the R sub-chains merge in
@@ -310,21 +321,30 @@ __global__ __launch_bounds__(Geo<H>::BLOCK) void k_bwd_large(BwdArgs a) {
     // issues its loads unconditionally (a load under a branch would make the
     // compiler drain every outstanding load at the join); the last one or
     // two batches are peeled.
-    RowBatch<H, FORM, D> ba, bb;
-    load(ba, 0);
-    int b = 0;
-    for (; b + 2 < nb; b += 2) {
-      load(bb, b + 1);
-      process(ba, b);
-      load(ba, b + 2);
-      process(bb, b + 1);
-    }
-    if (b + 1 < nb) {
-      load(bb, b + 1);
-      process(ba, b);
-      process(bb, b + 1);
+    if constexpr (BwdShape<H, FORM>::PIPE) {
+      RowBatch<H, FORM, D> ba, bb;
+      load(ba, 0);
+      int b = 0;
+      for (; b + 2 < nb; b += 2) {
+        load(bb, b + 1);
+        process(ba, b);
+        load(ba, b + 2);
+        process(bb, b + 1);
+      }
+      if (b + 1 < nb) {
+        load(bb, b + 1);
+        process(ba, b);
+        process(bb, b + 1);
+      } else {
+        process(ba, b);
+      }
     } else {
-      process(ba, b);
+      // one buffer: a batch of D rows per row group loads as one burst
+      for (int b = 0; b < nb; ++b) {
+        RowBatch<H, FORM, D> ba;
+        load(ba, b);
+        process(ba, b);
+      }
     }
     double dv[E];
 #pragma unroll
@@ -374,87 +394,122 @@ __global__ __launch_bounds__(kFoldThreads) void k_fold(const double* __restrict_
 
 // Small-row backward in one launch. Workgroups [0, row_grid) are row tasks
 // (dx, strided over row tiles of R rows); the rest are column tasks (dw),
-// strided over tiles of BLOCK/4 columns. A column-task thread (cv, kl) owns 8
-// columns and, per pass, chunk kl of the current fold group: it runs the R
-// sub-chains of its chunk exactly as k_bwd_large does, then the fold follows
-// k_fold's order through LDS. rstd is an input, so dw needs nothing from the
-// row tasks and no workgroup ever waits for another.
+// strided over column tiles. A column-task thread (cv, q, kl) owns 8 columns,
+// sub-chain q of chunk kl of the current fold group: it loads its sub-chain's
+// rows 8 at a time (one memory round trip per 8 rows) and runs Dot2 over them
+// in ascending order, exactly as k_bwd_large does. Through LDS, the chunk
+// partial is then 0.0 + d_0 + ... + d_{R-1} in sub-chain order, and the fold
+// follows k_fold's order. rstd is an input, so dw needs nothing from the row
+// tasks and no workgroup ever waits for another.
+// Workgroup size of the small path: the main kernel's, capped at 512 threads
+// (a row task needs whole row groups; the dw tree only needs the sub-chain
+// count R, which stays that of the main kernel).
+template <int H>
+struct SmallGeo {
+  static constexpr int BLOCK = Geo<H>::BLOCK > 768 ? 512 : Geo<H>::BLOCK;
+  static constexpr int RS = BLOCK / Geo<H>::TPR;  // rows per row-task tile
+  static_assert(RS >= 1 && RS * Geo<H>::TPR == BLOCK, "row tasks hold whole row groups");
+};
+
 template <int H, bool WF32, int FORM>
-__global__ __launch_bounds__(Geo<H>::BLOCK) void k_bwd_small(BwdArgs a, int row_grid) {
+__global__ __launch_bounds__(SmallGeo<H>::BLOCK) void k_bwd_small(BwdArgs a, int row_grid) {
   using G = Geo<H>;
-  constexpr int R = G::R, TPR = G::TPR;
+  constexpr int R = G::R, TPR = G::TPR, BLOCK = SmallGeo<H>::BLOCK, RS = SmallGeo<H>::RS;
+  constexpr int KL = kFoldGroup;               // chunk lanes: one pass = one fold group
+  constexpr int CV = BLOCK / (KL * R);         // column vectors per tile
+  constexpr int kTile = CV * 8;                // columns per tile
+  static_assert(CV >= 1 && CV * KL * R == BLOCK, "column-task layout");
+  static_assert(H % kTile == 0, "column tiles must cover the row exactly");
   __shared__ float slots[RowSum<H, 1>::kSlots];
-  __shared__ double part[kFoldGroup][Geo<H>::BLOCK / kFoldGroup * 8];
+  __shared__ double part[KL][R][kTile];
   if ((int)blockIdx.x < row_grid) {
     const int q = row_group<H>(), lane = threadIdx.x % TPR;
     int parity = 0;
     float wr[G::E];
     load_w<H, WF32>(a.w, lane, wr);
-    const int64_t tiles = (a.rows + R - 1) / R;
+    const int64_t tiles = (a.rows + RS - 1) / RS;
     for (int64_t t = blockIdx.x; t < tiles; t += row_grid) {
-      bool ok[1] = {t * R + q < a.rows};
-      int64_t row[1] = {ok[0] ? t * R + q : t * R};
+      bool ok[1] = {t * RS + q < a.rows};
+      int64_t row[1] = {ok[0] ? t * RS + q : t * RS};
       RowBatch<H, FORM, 1> rb;
       rb.load(a, row, ok, lane);
       rb.template compute_store<WF32>(a, wr, row, ok, q, lane, slots, parity, (NoDw*)nullptr);
     }
     return;
   }
-  constexpr int KL = kFoldGroup;              // chunk lanes: one pass = one fold group
-  constexpr int CV = G::BLOCK / KL;           // column vectors per tile
-  constexpr int kTile = CV * 8;               // columns per tile
-  static_assert(H % kTile == 0, "column tiles must cover the row exactly");
-  const int cv = threadIdx.x % CV, kl = threadIdx.x / CV;
+  const int cv = threadIdx.x % CV;
+  const int q = (threadIdx.x / CV) % R;
+  const int kl = threadIdx.x / (CV * R);
   const int col_grid = gridDim.x - row_grid;
   const int64_t C = a.chunk_rows;
-  const int64_t groups = (a.chunks + kFoldGroup - 1) / kFoldGroup;
+  const int64_t groups = (a.chunks + KL - 1) / KL;
   for (int tile = blockIdx.x - row_grid; tile < H / kTile; tile += col_grid) {
     const int c0 = tile * kTile + cv * 8;
     double total[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) total[i] = 0.0;
     for (int64_t g = 0; g < groups; ++g) {
-      const int64_t k = g * kFoldGroup + kl;
+      const int64_t k = g * KL + kl;
       if (k < a.chunks) {
-        double p[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] = 0.0;
         const int64_t r0 = k * C;
         const int64_t r1 = r0 + C < a.rows ? r0 + C : a.rows;
-        for (int qq = 0; qq < R; ++qq) {
-          Dot2 acc[8];
-          for (int64_t row = r0 + qq; row < r1; row += R) {
-            const float r = a.rstd[row];
-            float xf[8], gf[8], zf[8];
-            unpack8(ld16(a.x.p + row_off(a.x, row, a.heads) + c0), xf);
-            unpack8(ld16(a.dy.p + row_off(a.dy, row, a.heads) + c0), gf);
-            if constexpr (FORM == kGate) unpack8(ld16(a.e.p + row_off(a.e, row, a.heads) + c0), zf);
+        Dot2 acc[8];
+        for (int64_t rb0 = r0 + q; rb0 < r1; rb0 += 8 * (int64_t)R) {
+          constexpr int NB = 8;  // rows per round trip
+          uint4 xv[NB], gv[NB], zv[NB];
+          float rr[NB];
+          bool ok[NB];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              float b = r;
-              if constexpr (FORM == kGate) b = r * (zf[i] * sigmoid_f(zf[i]));
-              acc[i].add(gf[i] * xf[i], b);
-            }
+          for (int i = 0; i < NB; ++i) {
+            const int64_t row = rb0 + (int64_t)i * R;
+            ok[i] = row < r1;
+            const int64_t rc = ok[i] ? row : r0;
+            rr[i] = a.rstd[rc];
+            xv[i] = ld16(a.x.p + row_off(a.x, rc, a.heads) + c0);
+            gv[i] = ld16(a.dy.p + row_off(a.dy, rc, a.heads) + c0);
+            if constexpr (FORM == kGate) zv[i] = ld16(a.e.p + row_off(a.e, rc, a.heads) + c0);
           }
 #pragma unroll
-          for (int i = 0; i < 8; ++i) p[i] = p[i] + acc[i].value();
+          for (int i = 0; i < NB; ++i) {
+            if (!ok[i]) continue;
+            float xf[8], gf[8], zf[8];
+            unpack8(xv[i], xf);
+            unpack8(gv[i], gf);
+            if constexpr (FORM == kGate) unpack8(zv[i], zf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              float b = rr[i];
+              if constexpr (FORM == kGate) b = rr[i] * (zf[e] * sigmoid_f(zf[e]));
+              acc[e].add(gf[e] * xf[e], b);
+            }
+          }
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) part[kl][cv * 8 + i] = p[i];
+        for (int e = 0; e < 8; ++e) part[kl][q][cv * 8 + e] = acc[e].value();
       }
       __syncthreads();
-      if (kl == 0) {
-        const int64_t n = a.chunks - g * kFoldGroup < kFoldGroup ? a.chunks - g * kFoldGroup : kFoldGroup;
+      if (q == 0 && k < a.chunks) {
+        // chunk partial: 0.0 + d_0 + d_1 + ... in sub-chain order
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int e = 0; e < 8; ++e) {
+          double p = 0.0;
+          for (int qq = 0; qq < R; ++qq) p = p + part[kl][qq][cv * 8 + e];
+          part[kl][0][cv * 8 + e] = p;
+        }
+      }
+      __syncthreads();
+      if (q == 0 && kl == 0) {
+        const int64_t n = a.chunks - g * KL < KL ? a.chunks - g * KL : KL;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
           double s = 0.0;
-          for (int64_t kk = 0; kk < n; ++kk) s = s + part[kk][cv * 8 + i];
-          total[i] = total[i] + s;
+          for (int64_t kk = 0; kk < n; ++kk) s = s + part[kk][0][cv * 8 + e];
+          total[e] = total[e] + s;
         }
       }
       __syncthreads();
     }
-    if (kl == 0) {
+    if (q == 0 && kl == 0) {
       float4* o = reinterpret_cast<float4*>(a.dw + c0);
       o[0] = make_float4((float)total[0], (float)total[1], (float)total[2], (float)total[3]);
       o[1] = make_float4((float)total[4], (float)total[5], (float)total[6], (float)total[7]);

@@ -54,7 +54,8 @@ hipError_t launch_bwd_small(int H, bool w_f32, int form, const BwdArgs& a, int r
 
 // Grid sizes the kernels are written for (host-side planning).
 int fwd_rows_per_tile(int H);      // rows one workgroup handles per tile
-int bwd_rows_per_rowtask(int H);   // rows one small-path row workgroup handles
+int bwd_rows_per_rowtask(int H);   // R: row groups of the main kernel = sub-chains per chunk
+int small_rows_per_rowtask(int H); // rows one small-path row workgroup handles
 int small_col_tile(int H);         // columns per small-path column-task workgroup
 constexpr int kFoldGroup = 32;     // chunks per first-level group of the dw fold
 constexpr int kFoldTile = 32;      // columns per fold workgroup

@@ -176,15 +176,15 @@ def query(T, W, heads=1, det=1, launch=None):
     return plan
 
 
-@pytest.mark.parametrize("rows", [1, 15, 16, 17, 203, 16384, 16385, 65537, 98304, 131072,
+@pytest.mark.parametrize("rows", [1, 15, 16, 17, 203, 16384, 16385, 65537, 98304, 131072, 113536,
                                   786432, 3145728])
 def test_canonical_chunking(rows):
     p = query(rows, 512)
     C_ = p.chunk_rows
-    assert C_ % 16 == 0 and C_ >= 16
+    assert C_ >= 16
     assert p.chunks == -(-rows // C_) and p.chunks <= 1024
-    # smallest multiple of 16 that keeps the chunk count within 1024
-    assert C_ == 16 or -(-rows // (C_ - 16)) > 1024
+    # smallest chunk (>= 16 rows) that keeps the chunk count within 1024
+    assert C_ == 16 or -(-rows // (C_ - 1)) > 1024
     # the tree depends on the row count only: not on mode, launch or width
     for other in (query(rows, 4096, det=0), query(rows, 512, launch=R.Launch(5, 2, R.PATH_LARGE))):
         assert (other.chunk_rows, other.chunks) == (p.chunk_rows, p.chunks)
