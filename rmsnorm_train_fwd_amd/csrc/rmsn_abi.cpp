@@ -56,7 +56,7 @@ Span dense_span(const void* p, int64_t bytes) {
 // Byte extent of a strided BF16 row input: base .. last element + 1.
 Span row_span(const void* p, const rmsn_layout& L, int64_t st, int64_t sh) {
   if (!p || L.T == 0) return Span{};
-  const int64_t last = (L.T - 1) * st + (L.heads - 1) * (L.heads > 1 ? sh : 0) + L.width;
+  const int64_t last = (L.T - 1) * (L.T > 1 ? st : 0) + (L.heads - 1) * (L.heads > 1 ? sh : 0) + L.width;
   return dense_span(p, last * 2);
 }
 
@@ -77,6 +77,13 @@ rmsn_status check_layout(const rmsn_layout* L) {
       const int64_t need = (L->heads - 1) * (L->heads > 1 ? sh : 0) + L->width;
       if (st < need || st > kMaxStride) return RMSN_E_STRIDE;
       if (st % 8) return RMSN_E_ALIGN;
+    }
+    // The view's byte extent must fit the 48-bit address space (computed
+    // wide: T * stride_t alone can exceed 64 bits within the per-field bounds).
+    if (L->T > 0) {
+      const __int128 last = (__int128)(L->T - 1) * (L->T > 1 ? st : 0) +
+                            (__int128)(L->heads - 1) * (L->heads > 1 ? sh : 0) + L->width;
+      if (last * 2 > ((__int128)1 << 48)) return RMSN_E_SHAPE;
     }
   }
   return RMSN_OK;

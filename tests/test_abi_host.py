@@ -120,6 +120,10 @@ def test_stride_validation():
     assert fwd(lay(4, 512, st=-512), a["x"], None, a["w"], a["y"], None, a["rstd"]) == E_STRIDE
     # strides are ignored where they are unused (T == 1; heads == 1)
     assert fwd(lay(1, 512, st=3), a["x"], None, a["w"], a["y"], None, a["rstd"]) != E_STRIDE
+    # a view whose byte extent exceeds the address space (T * stride_t would
+    # overflow 64-bit arithmetic) is rejected, not wrapped around
+    huge = R.Layout((1 << 31) - 1, 1, 512, 1 << 40, 512, 1 << 40, 512)
+    assert fwd(huge, a["x"], None, a["w"], a["y"], None, a["rstd"]) == E_SHAPE
 
 
 def setup_bwd(T=8, W=512):
