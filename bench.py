@@ -24,7 +24,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 T_HEAD, H_HEAD = 131072, 4096
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_131072x4096.json")
-KERNEL_SOURCES = ["rmsn_kernels.hpp", "rmsn_device.hpp", "rmsn_bwd_large.hip"]
+KERNEL_SOURCES = ["rmsn_kernels.hpp", "rmsn_device.hpp", "rmsn_bwd_large.hip", "rmsn_launch.hpp", "rmsn_abi.cpp"]
 
 
 def bwd_bytes(T, H, w_bytes):
@@ -387,6 +387,9 @@ def traffic_report(fetch_dir, write_dir, out_json, out_md):
         return sum(v) / len(v)
 
     kr, kw = per(F, "k_bwd_large", ff), per(W, "k_bwd_large", wf)
+    import torch
+    import rmsnorm_train_fwd_amd as R
+    chunks = R.rmsnorm_train_bwd_query(torch.empty((T_HEAD, H_HEAD), dtype=torch.bfloat16), False).chunks
     fr, fw = per(F, "k_fold", ff), per(W, "k_fold", wf)
     total, alg = kr + kw + fr + fw, bwd_bytes(T_HEAD, H_HEAD, 4)
     out = {"kernel_hash": kernel_hash(),
@@ -424,7 +427,7 @@ Calibration with that copy of known size (1 GiB read, 1 GiB written): FETCH_SIZE
 Algorithmic: reads x, dy, rstd, w = {(4 * T_HEAD * H_HEAD + 4 * T_HEAD + 4 * H_HEAD) / 1e9:.4f} GB;
 writes dx, dw = {(2 * T_HEAD * H_HEAD + 4 * H_HEAD) / 1e9:.4f} GB; total {alg / 1e9:.4f} GB.
 Measured {total / 1e9:.4f} GB per call, {100 * (total / alg - 1):.2f}% above it: the FP64 chunk
-partials (1024 x 4096 x 8 B = 32 MiB) written by the main kernel and read back by the fold.
+partials ({chunks} x {H_HEAD} x 8 B = {chunks * H_HEAD * 8 / 2**20:.0f} MiB) written by the main kernel and read back by the fold.
 x, dy and dx are each moved once. Kernel sources hash: {out['kernel_hash']} (bench.py reports
 `traffic` only while the current sources hash to this value).
 """

@@ -114,9 +114,8 @@ typedef struct {
 typedef struct {
   int32_t path;          /* RMSN_PATH_SMALL or RMSN_PATH_LARGE */
   int64_t rows;          /* T * heads */
-  int64_t chunk_rows;    /* C: rows per canonical chunk of the dw tree */
-  int64_t chunks;        /* ceil(rows / C) */
-  int32_t subchains;     /* interleaved sub-chains per chunk (fixed per width) */
+  int64_t chunks;        /* K: chunks of the dw tree (see rmsnorm_train_bwd) */
+  int32_t subchains;     /* R: rows per tile = sub-chains per chunk (fixed per width) */
   int32_t fold_group;    /* chunks per first-level fold group */
   int32_t grid;          /* workgroups of the main (or single) launch */
   int32_t fold_grid;     /* workgroups of the fold launch (0 on the small path) */
@@ -139,17 +138,20 @@ rmsn_status rmsnorm_train_fwd(const void* x, const void* residual, const void* w
  * BF16 h of the forward in the residual form), the forward's rstd and w.
  * dh != NULL selects the residual form: the row output is grad_h = dh + dx
  * (one rounding), dh in the g strides ([C] "Residual rows").
- * deterministic != 0 ([C]): per column, rows are grouped into canonical
- *   chunks of C rows (C depends only on T*heads); inside a chunk, rows
- *   interleave into a fixed number of sub-chains (fixed per width), each
- *   summed in ascending row order with exact products (dy*x is exact in FP32,
- *   times rstd by an FMA-based TwoProduct) and TwoSum-compensated FP32
- *   accumulation; sub-chains merge in order in FP64; chunk partials fold in
- *   FP64 in a fixed two-level order; one rounding to FP32. The result is
- *   bit-identical for every grid, every path and every device.
- * deterministic == 0 ([D]): same chunking, FP32 block sums of dy*xhat over
- *   8 rows flushed into a TwoSum-compensated pair, FP64 combine. No bitwise
- *   guarantee is made for this mode.
+ * deterministic != 0 ([C]): per column, the rows form tiles of R
+ *   consecutive rows (R fixed per width) and the tiles are dealt in turn to K
+ *   chunks: chunk k holds tiles k, k+K, k+2K, ... K depends only on T*heads
+ *   and the width: ceil(tiles/8) when T*heads <= 256, otherwise min(tiles,
+ *   256), or min(tiles, 512) at width 5120. Row q of each of a chunk's tiles,
+ *   in ascending tile order, forms sub-chain q, summed with exact products
+ *   (dy*x is exact in FP32, times rstd by an FMA-based TwoProduct) and
+ *   TwoSum-compensated FP32 accumulation; the R sub-chains merge in order in
+ *   FP64; chunk partials fold in FP64 in a fixed two-level order (groups of
+ *   32 consecutive chunks, then the groups); one rounding to FP32. The result
+ *   is bit-identical for every grid, every path and every device.
+ * deterministic == 0 ([D]): same chunks and sub-chains, FP32 block sums of
+ *   dy*xhat over 8 rows of a sub-chain flushed into a TwoSum-compensated
+ *   pair, FP64 combine. No bitwise guarantee is made for this mode.
  * workspace: at least the bytes rmsnorm_train_bwd_query reports (0 on the
  *   small path; may then be NULL). Its contents on entry do not matter.     */
 rmsn_status rmsnorm_train_bwd(const void* dy, const void* x, const void* dh, const void* w,

@@ -49,7 +49,7 @@ class Launch(C.Structure):
 
 class BwdPlan(C.Structure):
     _fields_ = [
-        ("path", C.c_int32), ("rows", C.c_int64), ("chunk_rows", C.c_int64),
+        ("path", C.c_int32), ("rows", C.c_int64),
         ("chunks", C.c_int64), ("subchains", C.c_int32), ("fold_group", C.c_int32),
         ("grid", C.c_int32), ("fold_grid", C.c_int32), ("workspace_bytes", C.c_size_t),
     ]

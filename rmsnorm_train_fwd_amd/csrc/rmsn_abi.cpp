@@ -16,8 +16,8 @@ using namespace rmsn;
 
 constexpr int64_t kWidths[] = {256, 512, 1536, 2048, 4096, 5120, 6144};
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
-constexpr int64_t kMaxChunks = 1024;     // chunk partials per call (workspace bound)
-constexpr int64_t kMinChunkRows = 16;    // smallest chunk
+constexpr int64_t kSmallTreeRows = 256;  // row counts whose chunks hold at most ...
+constexpr int64_t kSmallTreeTiles = 8;   // ... this many tiles
 constexpr int64_t kMaxStride = int64_t(1) << 40;
 constexpr int32_t kMaxGrid = 1 << 24;
 
@@ -34,6 +34,11 @@ bool width_ok(int64_t w) {
 int rows_per_subchain_group(int64_t width) {  // R: row groups per workgroup
   return bwd_rows_per_rowtask((int)width);
 }
+
+// Chunks of the dw tree for a large row count: one per workgroup of the main
+// kernel that a 256-CU part holds at once (two per CU at width 5120, one
+// otherwise), so all chunks run in one round with no tail.
+int64_t max_chunks(int64_t width) { return width == 5120 ? 512 : 256; }
 
 struct Span {
   uintptr_t lo = 0, hi = 0;  // [lo, hi); empty if lo == hi
@@ -106,14 +111,16 @@ void make_plan(const rmsn_layout& L, int /*det*/, const rmsn_launch* o, rmsn_bwd
   memset(p, 0, sizeof *p);
   const int64_t rows = L.T * L.heads;
   p->rows = rows;
-  // Canonical chunking of the dw tree: depends on the row count only. The
-  // smallest C >= 16 with at most 1024 chunks, so large calls always have
-  // close to 1024 equal chunks (whole rounds of resident workgroups).
-  int64_t c = cdiv(rows, kMaxChunks);
-  if (c < kMinChunkRows) c = kMinChunkRows;
-  p->chunk_rows = c;
-  p->chunks = cdiv(rows, c);
-  p->subchains = rows_per_subchain_group(L.width);
+  // The dw tree: depends on the row count and the width only. Tiles of R
+  // rows are dealt to the chunks in turn. Small row counts: at most 8 tiles
+  // per chunk (one load round trip per sub-chain on the single-launch path);
+  // otherwise max_chunks(width) chunks, or one per tile if there are fewer.
+  const int64_t R = rows_per_subchain_group(L.width);
+  const int64_t tiles = cdiv(rows, R);
+  int64_t K = rows <= kSmallTreeRows ? cdiv(tiles, kSmallTreeTiles) : max_chunks(L.width);
+  if (K > tiles) K = tiles;
+  p->chunks = K;
+  p->subchains = (int32_t)R;
   p->fold_group = kFoldGroup;
   int path = o ? o->path : RMSN_PATH_AUTO;
   if (rows == 0) path = RMSN_PATH_SMALL;  // only dw = 0 to write
@@ -203,7 +210,6 @@ rmsn_status bwd_common(int form, const void* dy, const void* x, const void* e, c
   a.dw = dw;
   a.ws = static_cast<double*>(ws);
   a.rows = rows;
-  a.chunk_rows = plan.chunk_rows;
   a.chunks = plan.chunks;
   a.heads = (int32_t)L->heads;
   const bool wf32 = (w_dtype == RMSN_F32);

@@ -222,11 +222,13 @@ struct RowSum {
 
 // ------------------------------------------------------------ dw tree --
 //
-// Deterministic dw: the rows of a call are cut into canonical chunks of C rows
-// (C from the row count alone, see the host plan); inside chunk k the rows
-// k*C + q + i*R (i = 0, 1, ...) form sub-chain q, summed in ascending order by
-// Dot2 (TwoProduct + TwoSum, compensation in FP32); the chunk partial is
-// 0.0 + d_0 + d_1 + ... + d_{R-1} in FP64 with d_q = (double)s_q + (double)c_q;
+// Deterministic dw: the rows of a call form tiles of R consecutive rows (R
+// fixed per width), and the tiles are dealt to K chunks in turn: chunk k holds
+// tiles k, k + K, k + 2K, ... (K from the row count and the width alone, see
+// the host plan). Row q of each of chunk k's tiles, in ascending tile order,
+// forms sub-chain q, summed by Dot2 (TwoProduct + TwoSum, compensation in
+// FP32); the chunk partial is 0.0 + d_0 + d_1 + ... + d_{R-1} in FP64 with
+// d_q = (double)s_q + (double)c_q;
 // partials fold in FP64: consecutive groups of kFoldGroup chunks are summed in
 // ascending order from 0.0, then the group sums in ascending order from 0.0,
 // then one rounding to FP32. Every kernel below that produces dw follows this

@@ -264,10 +264,13 @@ struct BwdShape {
   static constexpr bool PIPE = kGateBurst ? true : Geo<H>::PIPE;
 };
 
-// Backward main kernel. Workgroup-strided over the canonical chunks of the dw
-// tree; inside a chunk, row group q walks rows k*C + q + i*R in ascending i,
-// D rows per batch, accumulating its sub-chain; the R sub-chains merge in
-// order through LDS in FP64 and the chunk partial goes to ws[k][:].
+// Backward main kernel. Workgroup-strided over the chunks of the dw tree. The
+// rows form tiles of R consecutive rows and chunk k holds the tiles k, k + K,
+// k + 2K, ... (K = a.chunks), so the workgroups in flight together stream one
+// contiguous window of each tensor. Row group q takes row q of each of the
+// chunk's tiles in ascending order, D tiles per batch, accumulating sub-chain
+// q; the R sub-chains merge in order through LDS in FP64 and the chunk partial
+// goes to ws[k][:].
 template <int H, bool WF32, int FORM, bool DET, int D>
 __global__ __launch_bounds__(Geo<H>::BLOCK) void k_bwd_large(BwdArgs a) {
   using G = Geo<H>;
@@ -279,21 +282,24 @@ __global__ __launch_bounds__(Geo<H>::BLOCK) void k_bwd_large(BwdArgs a) {
   int parity = 0;
   float wr[E];
   load_w<H, WF32>(a.w, lane, wr);
-  const int64_t C = a.chunk_rows;
-  const int nb = (int)((C + R * D - 1) / (R * D));
+  const int64_t K = a.chunks, tiles = (a.rows + R - 1) / R;
 
-  for (int64_t k = blockIdx.x; k < a.chunks; k += gridDim.x) {
-    const int64_t r0 = k * C;
-    const int64_t r1 = r0 + C < a.rows ? r0 + C : a.rows;
+  for (int64_t k = blockIdx.x; k < K; k += gridDim.x) {
+    // The chunk's tiles k, k + K, ... below `tiles`, D per batch. The host
+    // plans K <= tiles, so every chunk has at least one tile and r0 (row 0 of
+    // its first tile) is a real row; a chunk without tiles would contribute
+    // zeros, which is what it writes.
+    const int nb = k < tiles ? (int)(((tiles - k + K - 1) / K + D - 1) / D) : 0;
+    const int64_t r0 = k * R;
     Dot2 dacc[DET ? E : 1];
     Block8 bacc[DET ? 1 : E];
-    // Rows of batch b for this row group: k*C + (b*D + d)*R + q, d < D.
-    // Rows past the chunk end are masked and clamped to the chunk's first row.
+    // Rows of batch b for this row group: (k + (b*D + d)*K)*R + q, d < D.
+    // Rows past the end are masked and clamped to r0.
     auto rows_of = [&](int b, int64_t (&row)[D], bool (&ok)[D]) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
-        const int64_t rr = r0 + (int64_t)(b * D + d) * R + q;
-        ok[d] = rr < r1;
+        const int64_t rr = (k + (int64_t)(b * D + d) * K) * R + q;
+        ok[d] = rr < a.rows;
         row[d] = ok[d] ? rr : r0;
       }
     };
@@ -321,7 +327,9 @@ __global__ __launch_bounds__(Geo<H>::BLOCK) void k_bwd_large(BwdArgs a) {
     // issues its loads unconditionally (a load under a branch would make the
     // compiler drain every outstanding load at the join); the last one or
     // two batches are peeled.
-    if constexpr (BwdShape<H, FORM>::PIPE) {
+    if (nb == 0) {
+      // no tiles (not planned by the host): nothing to process
+    } else if constexpr (BwdShape<H, FORM>::PIPE) {
       RowBatch<H, FORM, D> ba, bb;
       load(ba, 0);
       int b = 0;
@@ -393,10 +401,11 @@ __global__ __launch_bounds__(kFoldThreads) void k_fold(const double* __restrict_
                                                        int64_t chunks);
 
 // Small-row backward in one launch. Workgroups [0, row_grid) are row tasks
-// (dx, strided over row tiles of R rows); the rest are column tasks (dw),
+// (dx, strided over row tiles of RS rows); the rest are column tasks (dw),
 // strided over column tiles. A column-task thread (cv, q, kl) owns 8 columns,
-// sub-chain q of chunk kl of the current fold group: it loads its sub-chain's
-// rows 8 at a time (one memory round trip per 8 rows) and runs Dot2 over them
+// sub-chain q of chunk kl of the current fold group: it loads row q of the
+// chunk's tiles 8 tiles at a time (one memory round trip; the tree gives a
+// chunk at most 8 tiles when the row count is small) and runs Dot2 over them
 // in ascending order, exactly as k_bwd_large does. Through LDS, the chunk
 // partial is then 0.0 + d_0 + ... + d_{R-1} in sub-chain order, and the fold
 // follows k_fold's order. rstd is an input, so dw needs nothing from the row
@@ -441,8 +450,8 @@ __global__ __launch_bounds__(SmallGeo<H>::BLOCK) void k_bwd_small(BwdArgs a, int
   const int q = (threadIdx.x / CV) % R;
   const int kl = threadIdx.x / (CV * R);
   const int col_grid = gridDim.x - row_grid;
-  const int64_t C = a.chunk_rows;
-  const int64_t groups = (a.chunks + KL - 1) / KL;
+  const int64_t K = a.chunks, tiles = (a.rows + R - 1) / R;
+  const int64_t groups = (K + KL - 1) / KL;
   for (int tile = blockIdx.x - row_grid; tile < H / kTile; tile += col_grid) {
     const int c0 = tile * kTile + cv * 8;
     double total[8];
@@ -450,19 +459,18 @@ __global__ __launch_bounds__(SmallGeo<H>::BLOCK) void k_bwd_small(BwdArgs a, int
     for (int i = 0; i < 8; ++i) total[i] = 0.0;
     for (int64_t g = 0; g < groups; ++g) {
       const int64_t k = g * KL + kl;
-      if (k < a.chunks) {
-        const int64_t r0 = k * C;
-        const int64_t r1 = r0 + C < a.rows ? r0 + C : a.rows;
+      if (k < K) {
+        const int64_t r0 = k * R;  // row 0 of the chunk's first tile (k < tiles)
         Dot2 acc[8];
-        for (int64_t rb0 = r0 + q; rb0 < r1; rb0 += 8 * (int64_t)R) {
-          constexpr int NB = 8;  // rows per round trip
+        constexpr int NB = 8;  // tiles per round trip
+        for (int64_t j0 = 0; k + j0 * K < tiles; j0 += NB) {
           uint4 xv[NB], gv[NB], zv[NB];
           float rr[NB];
           bool ok[NB];
 #pragma unroll
           for (int i = 0; i < NB; ++i) {
-            const int64_t row = rb0 + (int64_t)i * R;
-            ok[i] = row < r1;
+            const int64_t row = (k + (j0 + i) * K) * R + q;
+            ok[i] = row < a.rows;
             const int64_t rc = ok[i] ? row : r0;
             rr[i] = a.rstd[rc];
             xv[i] = ld16(a.x.p + row_off(a.x, rc, a.heads) + c0);
@@ -488,7 +496,7 @@ __global__ __launch_bounds__(SmallGeo<H>::BLOCK) void k_bwd_small(BwdArgs a, int
         for (int e = 0; e < 8; ++e) part[kl][q][cv * 8 + e] = acc[e].value();
       }
       __syncthreads();
-      if (q == 0 && k < a.chunks) {
+      if (q == 0 && k < K) {
         // chunk partial: 0.0 + d_0 + d_1 + ... in sub-chain order
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -499,7 +507,7 @@ __global__ __launch_bounds__(SmallGeo<H>::BLOCK) void k_bwd_small(BwdArgs a, int
       }
       __syncthreads();
       if (q == 0 && kl == 0) {
-        const int64_t n = a.chunks - g * KL < KL ? a.chunks - g * KL : KL;
+        const int64_t n = K - g * KL < KL ? K - g * KL : KL;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           double s = 0.0;

@@ -38,8 +38,7 @@ struct BwdArgs {
   float* dw;          // [H]
   double* ws;         // [chunks, H] FP64 chunk partials (large path)
   int64_t rows;
-  int64_t chunk_rows;
-  int64_t chunks;
+  int64_t chunks;     // K: chunks of the dw tree, 1 <= K <= ceil(rows / R) when rows > 0
   int32_t heads;
 };
 
@@ -54,7 +53,7 @@ hipError_t launch_bwd_small(int H, bool w_f32, int form, const BwdArgs& a, int r
 
 // Grid sizes the kernels are written for (host-side planning).
 int fwd_rows_per_tile(int H);      // rows one workgroup handles per tile
-int bwd_rows_per_rowtask(int H);   // R: row groups of the main kernel = sub-chains per chunk
+int bwd_rows_per_rowtask(int H);   // R: row groups of the main kernel = rows per tile = sub-chains per chunk
 int small_rows_per_rowtask(int H); // rows one small-path row workgroup handles
 int small_col_tile(int H);         // columns per small-path column-task workgroup
 constexpr int kFoldGroup = 32;     // chunks per first-level group of the dw fold

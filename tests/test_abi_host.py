@@ -180,24 +180,34 @@ def query(T, W, heads=1, det=1, launch=None):
     return plan
 
 
-@pytest.mark.parametrize("rows", [1, 15, 16, 17, 203, 16384, 16385, 65537, 98304, 131072, 113536,
-                                  786432, 3145728])
-def test_canonical_chunking(rows):
-    p = query(rows, 512)
-    C_ = p.chunk_rows
-    assert C_ >= 16
-    assert p.chunks == -(-rows // C_) and p.chunks <= 1024
-    # smallest chunk (>= 16 rows) that keeps the chunk count within 1024
-    assert C_ == 16 or -(-rows // (C_ - 1)) > 1024
-    # the tree depends on the row count only: not on mode, launch or width
-    for other in (query(rows, 4096, det=0), query(rows, 512, launch=R.Launch(5, 2, R.PATH_LARGE))):
-        assert (other.chunk_rows, other.chunks) == (p.chunk_rows, p.chunks)
+SUBCHAINS = {256: 16, 512: 8, 1536: 4, 2048: 4, 4096: 2, 5120: 1, 6144: 1}
+
+
+@pytest.mark.parametrize("W", [256, 512, 4096, 5120, 6144])
+@pytest.mark.parametrize("rows", [1, 15, 16, 17, 203, 256, 257, 300, 16384, 16385, 65537, 98304,
+                                  131072, 113536, 786432, 3145728])
+def test_dw_tree_chunking(rows, W):
+    p = query(rows, W)
+    assert p.subchains == SUBCHAINS[W] and p.fold_group == 32
+    tiles = -(-rows // p.subchains)
+    assert 1 <= p.chunks <= tiles          # every chunk holds at least one tile
+    if rows <= 256:
+        # as few chunks as hold at most 8 tiles each
+        assert p.chunks == -(-tiles // 8)
+    else:
+        # one chunk per workgroup a 256-CU part holds at once (two per CU at 5120)
+        assert p.chunks == min(tiles, 512 if W == 5120 else 256)
+    # the tree depends on the row count and the width only: not on the mode,
+    # the grid or the path
+    for other in (query(rows, W, det=0), query(rows, W, launch=R.Launch(5, 2, R.PATH_LARGE)),
+                  query(rows, W, launch=R.Launch(3, 1, R.PATH_SMALL))):
+        assert (other.chunks, other.subchains) == (p.chunks, p.subchains)
 
 
 def test_plan_headline_and_paths():
     p = query(131072, 4096)
-    assert (p.chunk_rows, p.chunks, p.subchains, p.fold_group) == (128, 1024, 2, 32)
-    assert p.workspace_bytes == 1024 * 4096 * 8 and p.grid == 1024 and p.fold_grid == 128
+    assert (p.chunks, p.subchains, p.fold_group) == (256, 2, 32)
+    assert p.workspace_bytes == 256 * 4096 * 8 and p.grid == 256 and p.fold_grid == 128
     s = query(8, 512)
     assert s.path == R.PATH_SMALL and s.workspace_bytes == 0 and s.subchains == 8
     assert query(4, 256, heads=24).subchains == 16

@@ -111,7 +111,7 @@ def test_config2_per_head_views(strides, w_dtype):
 @pytest.mark.parametrize("det", [False, True], ids=["nondet", "det"])
 @pytest.mark.parametrize("H", WIDTHS)
 def test_config3_large_path_elementwise_ragged(H, det):
-    # spans many chunks and a ragged last chunk, every row checked
+    # every chunk holds several tiles, the last tile is ragged; every row checked
     run_case(synth.make(4099, H, seed=1, w_dtype="f32"), det=det)
 
 
