@@ -450,26 +450,29 @@ __global__ __launch_bounds__(SmallGeo<H>::BLOCK) void k_bwd_small(BwdArgs a, int
   const int q = (threadIdx.x / CV) % R;
   const int kl = threadIdx.x / (CV * R);
   const int col_grid = gridDim.x - row_grid;
-  const int64_t K = a.chunks, tiles = (a.rows + R - 1) / R;
+  const int64_t K = a.chunks;
   const int64_t groups = (K + KL - 1) / KL;
   for (int tile = blockIdx.x - row_grid; tile < H / kTile; tile += col_grid) {
     const int c0 = tile * kTile + cv * 8;
-    double total[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) total[i] = 0.0;
+    double total = 0.0;  // column c0 + kl, on threads (cv, q = 0, kl < 8)
     for (int64_t g = 0; g < groups; ++g) {
       const int64_t k = g * KL + kl;
       if (k < K) {
-        const int64_t r0 = k * R;  // row 0 of the chunk's first tile (k < tiles)
+        // Row q of the chunk's tiles: rb + i*step; rb - q is row 0 of the
+        // current tile, which exists while it is below the row count. Masked
+        // rows load r0 (row 0 of the chunk's first tile, a real row whenever
+        // the loop runs) and are skipped.
+        const int64_t r0 = k * R;
+        const int64_t step = K * R;
         Dot2 acc[8];
         constexpr int NB = 8;  // tiles per round trip
-        for (int64_t j0 = 0; k + j0 * K < tiles; j0 += NB) {
+        for (int64_t rb = r0 + q; rb - q < a.rows; rb += NB * step) {
           uint4 xv[NB], gv[NB], zv[NB];
           float rr[NB];
           bool ok[NB];
 #pragma unroll
           for (int i = 0; i < NB; ++i) {
-            const int64_t row = (k + (j0 + i) * K) * R + q;
+            const int64_t row = rb + i * step;
             ok[i] = row < a.rows;
             const int64_t rc = ok[i] ? row : r0;
             rr[i] = a.rstd[rc];
@@ -506,22 +509,25 @@ __global__ __launch_bounds__(SmallGeo<H>::BLOCK) void k_bwd_small(BwdArgs a, int
         }
       }
       __syncthreads();
-      if (q == 0 && kl == 0) {
-        const int64_t n = K - g * KL < KL ? K - g * KL : KL;
+      // Group fold, one thread per column (thread (cv, 0, kl) takes column
+      // c0 + kl): the group's chunk partials in ascending order from 0.0,
+      // read from LDS 8 at a time ahead of the adds.
+      if (q == 0 && kl < 8) {
+        const int n = (int)(K - g * KL < KL ? K - g * KL : KL);
+        double s = 0.0;
+        for (int k0 = 0; k0 < n; k0 += 8) {
+          double v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          double s = 0.0;
-          for (int64_t kk = 0; kk < n; ++kk) s = s + part[kk][0][cv * 8 + e];
-          total[e] = total[e] + s;
+          for (int i = 0; i < 8; ++i) v[i] = k0 + i < n ? part[k0 + i][0][cv * 8 + kl] : 0.0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (k0 + i < n) s = s + v[i];
         }
+        total = total + s;
       }
       __syncthreads();
     }
-    if (q == 0 && kl == 0) {
-      float4* o = reinterpret_cast<float4*>(a.dw + c0);
-      o[0] = make_float4((float)total[0], (float)total[1], (float)total[2], (float)total[3]);
-      o[1] = make_float4((float)total[4], (float)total[5], (float)total[6], (float)total[7]);
-    }
+    if (q == 0 && kl < 8) a.dw[c0 + kl] = (float)total;
   }
 }
 
