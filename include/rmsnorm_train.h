@@ -141,8 +141,8 @@ rmsn_status rmsnorm_train_fwd(const void* x, const void* residual, const void* w
  * deterministic != 0 ([C]): per column, the rows form tiles of R
  *   consecutive rows (R fixed per width) and the tiles are dealt in turn to K
  *   chunks: chunk k holds tiles k, k+K, k+2K, ... K depends only on T*heads
- *   and the width: ceil(tiles/8) when T*heads <= 256, otherwise min(tiles,
- *   256), or min(tiles, 512) at width 5120. Row q of each of a chunk's tiles,
+ *   and the width: ceil(tiles/8) when T*heads <= 256, otherwise
+ *   min(tiles, 256). Row q of each of a chunk's tiles,
  *   in ascending tile order, forms sub-chain q, summed with exact products
  *   (dy*x is exact in FP32, times rstd by an FMA-based TwoProduct) and
  *   TwoSum-compensated FP32 accumulation; the R sub-chains merge in order in

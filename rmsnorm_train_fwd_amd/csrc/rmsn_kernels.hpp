@@ -254,14 +254,17 @@ struct RowBatch {
 };
 
 // Batch shape of the backward main kernel for one form: the width's default,
-// except that the gated form (which also carries z) keeps to one row per
-// batch, pipelined, where the default is a multi-row burst (the burst would
-// not fit in registers).
+// except that (a) the gated form (which also carries z) keeps to one row per
+// batch, pipelined, where the default is a multi-row burst, and (b) with two
+// vectors per thread (V = 2) the residual and gated forms (which carry dh or
+// z) take one row per batch without the second buffer: both would not fit in
+// registers otherwise.
 template <int H, int FORM>
 struct BwdShape {
+  static constexpr bool kWide = FORM != kPlain && Geo<H>::V > 1;
   static constexpr bool kGateBurst = FORM == kGate && !Geo<H>::PIPE;
-  static constexpr int D = kGateBurst ? 1 : Geo<H>::D;
-  static constexpr bool PIPE = kGateBurst ? true : Geo<H>::PIPE;
+  static constexpr int D = (kWide || kGateBurst) ? 1 : Geo<H>::D;
+  static constexpr bool PIPE = kWide ? false : (kGateBurst ? true : Geo<H>::PIPE);
 };
 
 // Backward main kernel. Workgroup-strided over the chunks of the dw tree. The

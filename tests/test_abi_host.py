@@ -180,7 +180,7 @@ def query(T, W, heads=1, det=1, launch=None):
     return plan
 
 
-SUBCHAINS = {256: 16, 512: 8, 1536: 4, 2048: 4, 4096: 2, 5120: 1, 6144: 1}
+SUBCHAINS = {256: 16, 512: 8, 1536: 4, 2048: 4, 4096: 2, 5120: 2, 6144: 1}
 
 
 @pytest.mark.parametrize("W", [256, 512, 4096, 5120, 6144])
@@ -195,8 +195,8 @@ def test_dw_tree_chunking(rows, W):
         # as few chunks as hold at most 8 tiles each
         assert p.chunks == -(-tiles // 8)
     else:
-        # one chunk per workgroup a 256-CU part holds at once (two per CU at 5120)
-        assert p.chunks == min(tiles, 512 if W == 5120 else 256)
+        # one chunk per workgroup a 256-CU part holds at once (one per CU)
+        assert p.chunks == min(tiles, 256)
     # the tree depends on the row count and the width only: not on the mode,
     # the grid or the path
     for other in (query(rows, W, det=0), query(rows, W, launch=R.Launch(5, 2, R.PATH_LARGE)),

@@ -37,6 +37,7 @@ CASES = [
     (203, 1536, 1, "plain"), (257, 2048, 1, "plain"), (1000, 5120, 1, "plain"),
     (4099, 4096, 1, "plain"), (33, 256, 24, "plain"), (300, 512, 1, "residual"),
     (129, 4096, 1, "gate"), (17, 6144, 1, "residual"), (600, 256, 4, "gate"),
+    (777, 5120, 1, "residual"), (300, 5120, 1, "gate"), (2000, 1536, 1, "gate"),
 ]
 
 

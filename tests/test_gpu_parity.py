@@ -165,15 +165,22 @@ def test_config5_gate_larger(T):
              nsample=48)
 
 
+@pytest.mark.parametrize("det", [True, False], ids=["det", "nondet"])
 @pytest.mark.parametrize("H", (256, 512, 1536, 2048, 5120, 6144))
-def test_gate_other_widths(H):
-    run_case(synth.make(300, H, seed=4, w_dtype="f32", form="gate"), det=True, form="gate")
+def test_gate_other_widths(H, det):
+    # 300 rows: main kernel + fold; 4099 rows: several tiles per chunk
+    run_case(synth.make(300, H, seed=4, w_dtype="f32", form="gate"), det=det, form="gate")
+    run_case(synth.make(4099, H, seed=5, w_dtype="f32", form="gate"), det=det, form="gate",
+             nsample=48)
 
 
-@pytest.mark.parametrize("H", (256, 512, 4096))
-def test_residual_other_widths(H):
-    run_case(synth.make(300, H, seed=4, w_dtype="bf16", form="residual"), det=True,
+@pytest.mark.parametrize("det", [True, False], ids=["det", "nondet"])
+@pytest.mark.parametrize("H", (256, 512, 1536, 4096, 5120))
+def test_residual_other_widths(H, det):
+    run_case(synth.make(300, H, seed=4, w_dtype="bf16", form="residual"), det=det,
              form="residual")
+    run_case(synth.make(4099, H, seed=5, w_dtype="f32", form="residual"), det=det,
+             form="residual", nsample=48)
 
 
 # ------------------------------------------------------------ input families --
