@@ -300,7 +300,7 @@ static rmsn_status fwd_common(int form, const void* x, const void* e, const void
   a.rows = rows;
   a.heads = (int32_t)L->heads;
   a.eps = eps;
-  const int64_t tiles = cdiv(rows, fwd_rows_per_tile((int)W));
+  const int64_t tiles = cdiv(rows, fwd_rows_per_tile((int)W, form));
   const int grid = (int)(tiles < kMaxGrid ? tiles : kMaxGrid);
   hipError_t err = launch_fwd((int)W, w_dtype == RMSN_F32, form, a, grid, as_stream(stream));
   return err == hipSuccess ? RMSN_OK : RMSN_E_HIP;

@@ -127,10 +127,12 @@ __device__ __forceinline__ float lane_sum(float v) {
 // reads TPR*16 contiguous bytes. A workgroup of BLOCK = TPR*R threads holds R
 // row groups, which work on R different rows at a time; in the backward main
 // kernel each row group takes D rows per batch, with the next batch's loads in
-// flight during the current one (PIPE) or not. The shapes keep each
-// thread at 8 columns: per-column state (weight, dw
-// accumulators) lives in registers, and fewer columns per thread means more
-// waves in flight.
+// flight during the current one (PIPE) or not. Per-column state (weight, dw
+// accumulators) lives in registers; fewer columns per thread means more waves
+// in flight, more columns means fewer, larger row groups. Cfg is the
+// backward's shape (its R is the sub-chain count of the dw tree); the
+// forward's (FwdCfg, with the kernels) is the same except where measurement
+// chose otherwise.
 template <int H> struct Cfg;
 template <> struct Cfg<256>  { static constexpr int TPR = 32,  V = 1, R = 16, D = 2; static constexpr bool PIPE = true; };
 template <> struct Cfg<512>  { static constexpr int TPR = 64,  V = 1, R = 8,  D = 4; static constexpr bool PIPE = false; };
@@ -140,38 +142,48 @@ template <> struct Cfg<4096> { static constexpr int TPR = 512, V = 1, R = 2,  D 
 template <> struct Cfg<5120> { static constexpr int TPR = 320, V = 2, R = 2,  D = 1; static constexpr bool PIPE = true; };
 template <> struct Cfg<6144> { static constexpr int TPR = 768, V = 1, R = 1,  D = 4; static constexpr bool PIPE = false; };
 
-template <int H>
-struct Geo {
-  static constexpr int TPR = Cfg<H>::TPR;
-  static constexpr int V = Cfg<H>::V;
-  static constexpr int R = Cfg<H>::R;              // row groups per workgroup
+
+template <int H_, class C>
+struct GeoOf {
+  static constexpr int H = H_;
+  static constexpr int TPR = C::TPR;
+  static constexpr int V = C::V;
+  static constexpr int R = C::R;                   // row groups per workgroup
   static constexpr int BLOCK = TPR * R;            // workgroup size
   static constexpr int LANES = TPR < 64 ? TPR : 64;
   static constexpr int WPR = TPR / LANES;          // waves per row group
   static constexpr int E = 8 * V;                  // elements per thread
-  static constexpr int D = Cfg<H>::D;              // rows per row group per backward batch
-  static constexpr bool PIPE = Cfg<H>::PIPE;       // backward: next batch loads during this one
+  static constexpr int D = C::D;                   // rows per row group per backward batch
+  static constexpr bool PIPE = C::PIPE;            // backward: next batch loads during this one
   static_assert(TPR * V * 8 == H, "layout must tile the row exactly");
   static_assert(TPR % 64 == 0 || TPR == 32, "row groups are half waves or whole waves");
   static_assert(BLOCK <= 1024 && BLOCK % 32 == 0, "workgroup size");
 };
 
+template <int H> using Geo = GeoOf<H, Cfg<H>>;  // backward
+
 // Row group of this thread. With whole-wave row groups it is the same for
 // every lane of a wave; saying so (readfirstlane) lets the compiler keep row
 // indices, row addresses and rstd in scalar registers.
-template <int H>
+template <class G>
 __device__ __forceinline__ int row_group() {
-  const int q = threadIdx.x / Geo<H>::TPR;
-  if constexpr (Geo<H>::TPR >= 64) return __builtin_amdgcn_readfirstlane(q);
+  const int q = threadIdx.x / G::TPR;
+  if constexpr (G::TPR >= 64) return __builtin_amdgcn_readfirstlane(q);
   else return q;
 }
 
+// First element of vector v of a lane.
+template <class G>
+__device__ __forceinline__ int elem0(int v, int lane) {
+  return (v * G::TPR + lane) * 8;
+}
+
 // Weight in registers: the E elements a thread owns, as FP32.
-template <int H, bool WF32>
-__device__ __forceinline__ void load_w(const void* w, int lane, float (&wr)[Geo<H>::E]) {
-  constexpr int TPR = Geo<H>::TPR;
+template <class G, bool WF32>
+__device__ __forceinline__ void load_w(const void* w, int lane, float (&wr)[G::E]) {
+  constexpr int TPR = G::TPR;
 #pragma unroll
-  for (int v = 0; v < Geo<H>::V; ++v) {
+  for (int v = 0; v < G::V; ++v) {
     const int e0 = (v * TPR + lane) * 8;
     if constexpr (WF32) {
       const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(w) + e0);
@@ -192,14 +204,14 @@ __device__ __forceinline__ void load_w(const void* w, int lane, float (&wr)[Geo<
 // only. Wider row groups add the per-wave sums through LDS in wave order
 // ((w0 + w1) + w2) + ..., with two alternating slot sets so that one barrier
 // per call suffices. All threads of the workgroup must call it together.
-template <int H, int D>
+template <class G, int D>
 struct RowSum {
-  static constexpr int R = Geo<H>::R, WPR = Geo<H>::WPR;
+  static constexpr int R = G::R, WPR = G::WPR;
   static constexpr int kSlots = (WPR > 1) ? 2 * R * WPR * D : 1;
 
   __device__ static void run(float (&v)[D], float* slots, int& parity, int q, int lane) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) v[d] = lane_sum<Geo<H>::LANES>(v[d]);
+    for (int d = 0; d < D; ++d) v[d] = lane_sum<G::LANES>(v[d]);
     if constexpr (WPR > 1) {
       float* s = slots + (parity * R + q) * WPR * D;
       const int wv = lane / 64;

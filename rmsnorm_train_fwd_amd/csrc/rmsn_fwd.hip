@@ -9,9 +9,11 @@ constexpr int kFwdRPG = 2;  // rows per row group per tile
 template <int H, bool WF32>
 hipError_t fwd_form(int form, const FwdArgs& a, int grid, hipStream_t s) {
   switch (form) {
-    case kPlain: k_fwd<H, WF32, kPlain, kFwdRPG><<<grid, Geo<H>::BLOCK, 0, s>>>(a); break;
-    case kResidual: k_fwd<H, WF32, kResidual, kFwdRPG><<<grid, Geo<H>::BLOCK, 0, s>>>(a); break;
-    case kGate: k_fwd<H, WF32, kGate, kFwdRPG><<<grid, Geo<H>::BLOCK, 0, s>>>(a); break;
+    case kPlain: k_fwd<H, WF32, kPlain, kFwdRPG><<<grid, FGeo<H, kPlain>::BLOCK, 0, s>>>(a); break;
+    case kResidual:
+      k_fwd<H, WF32, kResidual, kFwdRPG><<<grid, FGeo<H, kResidual>::BLOCK, 0, s>>>(a);
+      break;
+    case kGate: k_fwd<H, WF32, kGate, kFwdRPG><<<grid, FGeo<H, kGate>::BLOCK, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -23,15 +25,25 @@ hipError_t fwd_width(bool w_f32, int form, const FwdArgs& a, int grid, hipStream
 }
 }  // namespace
 
-int fwd_rows_per_tile(int H) {
+template <int H>
+int fwd_rows_per_tile_w(int form) {
+  switch (form) {
+    case kPlain: return FGeo<H, kPlain>::R * kFwdRPG;
+    case kResidual: return FGeo<H, kResidual>::R * kFwdRPG;
+    case kGate: return FGeo<H, kGate>::R * kFwdRPG;
+    default: return 0;
+  }
+}
+
+int fwd_rows_per_tile(int H, int form) {
   switch (H) {
-    case 256: return Geo<256>::R * kFwdRPG;
-    case 512: return Geo<512>::R * kFwdRPG;
-    case 1536: return Geo<1536>::R * kFwdRPG;
-    case 2048: return Geo<2048>::R * kFwdRPG;
-    case 4096: return Geo<4096>::R * kFwdRPG;
-    case 5120: return Geo<5120>::R * kFwdRPG;
-    case 6144: return Geo<6144>::R * kFwdRPG;
+    case 256: return fwd_rows_per_tile_w<256>(form);
+    case 512: return fwd_rows_per_tile_w<512>(form);
+    case 1536: return fwd_rows_per_tile_w<1536>(form);
+    case 2048: return fwd_rows_per_tile_w<2048>(form);
+    case 4096: return fwd_rows_per_tile_w<4096>(form);
+    case 5120: return fwd_rows_per_tile_w<5120>(form);
+    case 6144: return fwd_rows_per_tile_w<6144>(form);
     default: return 0;
   }
 }

@@ -22,10 +22,16 @@ __device__ __forceinline__ int64_t row_off(const RowIn& in, int64_t row, int hea
   return (int64_t)t * in.stride_t + (int64_t)h * in.stride_h;
 }
 
-template <int H>
-__device__ __forceinline__ int elem0(int v, int lane) {
-  return (v * Geo<H>::TPR + lane) * 8;
-}
+
+// Forward shape per width and form: the backward's, except the gated form at
+// 5120, which keeps one 640-thread row group (8 columns per thread) where the
+// other forms use two 320-thread row groups.
+template <int H, int FORM> struct FwdCfg : Cfg<H> {};
+template <> struct FwdCfg<5120, kGate> {
+  static constexpr int TPR = 640, V = 1, R = 1, D = 1;
+  static constexpr bool PIPE = true;
+};
+template <int H, int FORM> using FGeo = GeoOf<H, FwdCfg<H, FORM>>;
 
 // ------------------------------------------------------------------ forward --
 //
@@ -36,14 +42,14 @@ __device__ __forceinline__ int elem0(int v, int lane) {
 // differ by more than 16, and then the smaller one is far below half a BF16
 // ulp, so the result is the rounded exact sum), and the norm reads that h.
 template <int H, bool WF32, int FORM, int RPG>
-__global__ __launch_bounds__(Geo<H>::BLOCK) void k_fwd(FwdArgs a) {
-  using G = Geo<H>;
+__global__ __launch_bounds__((FGeo<H, FORM>::BLOCK)) void k_fwd(FwdArgs a) {
+  using G = FGeo<H, FORM>;
   constexpr int R = G::R, V = G::V, E = G::E;
-  const int q = row_group<H>(), lane = threadIdx.x % G::TPR;
-  __shared__ float slots[RowSum<H, RPG>::kSlots];
+  const int q = row_group<G>(), lane = threadIdx.x % G::TPR;
+  __shared__ float slots[RowSum<G, RPG>::kSlots];
   int parity = 0;
   float wr[E];
-  load_w<H, WF32>(a.w, lane, wr);
+  load_w<G, WF32>(a.w, lane, wr);
 
   const int64_t tiles = (a.rows + R * RPG - 1) / (R * RPG);
   for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
@@ -58,9 +64,9 @@ __global__ __launch_bounds__(Geo<H>::BLOCK) void k_fwd(FwdArgs a) {
       const int64_t eo = ok[i] && FORM != kPlain ? row_off(a.e, row[i], a.heads) : 0;
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        xv[i][v] = ok[i] ? ld16_stream(a.x.p + xo + elem0<H>(v, lane)) : make_uint4(0, 0, 0, 0);
+        xv[i][v] = ok[i] ? ld16_stream(a.x.p + xo + elem0<G>(v, lane)) : make_uint4(0, 0, 0, 0);
         if constexpr (FORM != kPlain)
-          ev[i][v] = ok[i] ? ld16_stream(a.e.p + eo + elem0<H>(v, lane)) : make_uint4(0, 0, 0, 0);
+          ev[i][v] = ok[i] ? ld16_stream(a.e.p + eo + elem0<G>(v, lane)) : make_uint4(0, 0, 0, 0);
       }
     }
     float xf[RPG][E];
@@ -77,7 +83,7 @@ __global__ __launch_bounds__(Geo<H>::BLOCK) void k_fwd(FwdArgs a) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) f[k] = f[k] + r8[k];
           const uint4 hb = pack8(f);
-          if (ok[i]) st16_stream(a.h + row[i] * H + elem0<H>(v, lane), hb);
+          if (ok[i]) st16_stream(a.h + row[i] * H + elem0<G>(v, lane), hb);
           unpack8(hb, f);  // the norm reads the rounded h
         }
 #pragma unroll
@@ -88,7 +94,7 @@ __global__ __launch_bounds__(Geo<H>::BLOCK) void k_fwd(FwdArgs a) {
       for (int k = 0; k < E; ++k) s = __builtin_fmaf(xf[i][k], xf[i][k], s);
       ss[i] = s;
     }
-    RowSum<H, RPG>::run(ss, slots, parity, q, lane);
+    RowSum<G, RPG>::run(ss, slots, parity, q, lane);
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
       const float r = 1.0f / __builtin_sqrtf(ss[i] / (float)H + a.eps);
@@ -103,7 +109,7 @@ __global__ __launch_bounds__(Geo<H>::BLOCK) void k_fwd(FwdArgs a) {
           if constexpr (FORM == kGate) t = t * (zf[k] * sigmoid_f(zf[k]));
           f[k] = t;
         }
-        if (ok[i]) st16_stream(a.y + row[i] * H + elem0<H>(v, lane), pack8(f));
+        if (ok[i]) st16_stream(a.y + row[i] * H + elem0<G>(v, lane), pack8(f));
       }
       if (ok[i] && lane == 0) a.rstd[row[i]] = r;
     }
@@ -121,7 +127,8 @@ struct NoDw {};  // accumulator policy of row tasks that only write dx
 
 template <int H, int FORM, int D>
 struct RowBatch {
-  static constexpr int V = Geo<H>::V, E = Geo<H>::E;
+  using G = Geo<H>;
+  static constexpr int V = G::V, E = G::E;
   uint4 xv[D][V], gv[D][V], ev[D][V];
   float r[D];
 
@@ -139,7 +146,7 @@ struct RowBatch {
       r[d] = a.rstd[row[d]];
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        const int e0 = elem0<H>(v, lane);
+        const int e0 = elem0<G>(v, lane);
         xv[d][v] = ld16_stream(a.x.p + xo + e0);
         gv[d][v] = ld16_stream(a.dy.p + go + e0);
         if constexpr (FORM != kPlain) ev[d][v] = ld16_stream(a.e.p + eo + e0);
@@ -218,7 +225,7 @@ struct RowBatch {
         }
       }
     }
-    RowSum<H, D>::run(dot, slots, parity, q, lane);
+    RowSum<G, D>::run(dot, slots, parity, q, lane);
     opaque();
 #pragma unroll
     for (int d = 0; d < D; ++d) {
@@ -245,7 +252,7 @@ struct RowBatch {
         // Unconditional: a masked entry holds a copy of a real row of the
         // same call (its index was clamped to that row), so it stores the very
         // bytes that row's own pass stores; no branch around the stores.
-        const int64_t o = row[d] * H + elem0<H>(v, lane);
+        const int64_t o = row[d] * H + elem0<G>(v, lane);
         st16_stream(a.dx + o, pack8(out));
         if constexpr (FORM == kGate) st16_stream(a.dz + o, pack8(dz));
       }
@@ -279,12 +286,12 @@ __global__ __launch_bounds__(Geo<H>::BLOCK) void k_bwd_large(BwdArgs a) {
   using G = Geo<H>;
   constexpr int R = G::R, V = G::V, E = G::E, TPR = G::TPR;
   static_assert(8 % D == 0, "a batch must not straddle an 8-row block");
-  const int q = row_group<H>(), lane = threadIdx.x % TPR;
-  __shared__ float slots[RowSum<H, D>::kSlots];
+  const int q = row_group<G>(), lane = threadIdx.x % TPR;
+  __shared__ float slots[RowSum<G, D>::kSlots];
   __shared__ double merge[R > 1 ? H : 1];
   int parity = 0;
   float wr[E];
-  load_w<H, WF32>(a.w, lane, wr);
+  load_w<G, WF32>(a.w, lane, wr);
   const int64_t K = a.chunks, tiles = (a.rows + R - 1) / R;
 
   for (int64_t k = blockIdx.x; k < K; k += gridDim.x) {
@@ -371,7 +378,7 @@ __global__ __launch_bounds__(Geo<H>::BLOCK) void k_bwd_large(BwdArgs a) {
     if constexpr (R == 1) {
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        double2* o = reinterpret_cast<double2*>(out + elem0<H>(v, lane));
+        double2* o = reinterpret_cast<double2*>(out + elem0<G>(v, lane));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           o[i] = make_double2(0.0 + dv[v * 8 + 2 * i], 0.0 + dv[v * 8 + 2 * i + 1]);
@@ -384,7 +391,7 @@ __global__ __launch_bounds__(Geo<H>::BLOCK) void k_bwd_large(BwdArgs a) {
           for (int v = 0; v < V; ++v)
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-              double& m = merge[elem0<H>(v, lane) + i];
+              double& m = merge[elem0<G>(v, lane) + i];
               m = (qq == 0 ? 0.0 : m) + dv[v * 8 + i];
             }
         }
@@ -432,13 +439,13 @@ __global__ __launch_bounds__(SmallGeo<H>::BLOCK) void k_bwd_small(BwdArgs a, int
   constexpr int kTile = CV * 8;                // columns per tile
   static_assert(CV >= 1 && CV * KL * R == BLOCK, "column-task layout");
   static_assert(H % kTile == 0, "column tiles must cover the row exactly");
-  __shared__ float slots[RowSum<H, 1>::kSlots];
+  __shared__ float slots[RowSum<G, 1>::kSlots];
   __shared__ double part[KL][R][kTile];
   if ((int)blockIdx.x < row_grid) {
-    const int q = row_group<H>(), lane = threadIdx.x % TPR;
+    const int q = row_group<G>(), lane = threadIdx.x % TPR;
     int parity = 0;
     float wr[G::E];
-    load_w<H, WF32>(a.w, lane, wr);
+    load_w<G, WF32>(a.w, lane, wr);
     const int64_t tiles = (a.rows + RS - 1) / RS;
     for (int64_t t = blockIdx.x; t < tiles; t += row_grid) {
       bool ok[1] = {t * RS + q < a.rows};

@@ -52,7 +52,7 @@ hipError_t launch_bwd_small(int H, bool w_f32, int form, const BwdArgs& a, int r
                             int col_grid, hipStream_t s);
 
 // Grid sizes the kernels are written for (host-side planning).
-int fwd_rows_per_tile(int H);      // rows one workgroup handles per tile
+int fwd_rows_per_tile(int H, int form);  // rows one workgroup handles per tile
 int bwd_rows_per_rowtask(int H);   // R: row groups of the main kernel = rows per tile = sub-chains per chunk
 int small_rows_per_rowtask(int H); // rows one small-path row workgroup handles
 int small_col_tile(int H);         // columns per small-path column-task workgroup
