@@ -135,12 +135,12 @@ __device__ __forceinline__ float lane_sum(float v) {
 // chose otherwise.
 template <int H> struct Cfg;
 template <> struct Cfg<256>  { static constexpr int TPR = 32,  V = 1, R = 16, D = 2; static constexpr bool PIPE = true; };
-template <> struct Cfg<512>  { static constexpr int TPR = 64,  V = 1, R = 8,  D = 4; static constexpr bool PIPE = false; };
+template <> struct Cfg<512>  { static constexpr int TPR = 64,  V = 1, R = 8,  D = 1; static constexpr bool PIPE = true; };
 template <> struct Cfg<1536> { static constexpr int TPR = 192, V = 1, R = 4,  D = 2; static constexpr bool PIPE = true; };
 template <> struct Cfg<2048> { static constexpr int TPR = 256, V = 1, R = 4,  D = 1; static constexpr bool PIPE = true; };
 template <> struct Cfg<4096> { static constexpr int TPR = 512, V = 1, R = 2,  D = 1; static constexpr bool PIPE = true; };
 template <> struct Cfg<5120> { static constexpr int TPR = 320, V = 2, R = 2,  D = 1; static constexpr bool PIPE = true; };
-template <> struct Cfg<6144> { static constexpr int TPR = 768, V = 1, R = 1,  D = 4; static constexpr bool PIPE = false; };
+template <> struct Cfg<6144> { static constexpr int TPR = 768, V = 1, R = 1,  D = 1; static constexpr bool PIPE = true; };
 
 
 template <int H_, class C>

@@ -262,16 +262,22 @@ struct RowBatch {
 
 // Batch shape of the backward main kernel for one form: the width's default,
 // except that (a) the gated form (which also carries z) keeps to one row per
-// batch, pipelined, where the default is a multi-row burst, and (b) with two
+// batch, pipelined, where the default is a multi-row burst; (b) with two
 // vectors per thread (V = 2) the residual and gated forms (which carry dh or
-// z) take one row per batch without the second buffer: both would not fit in
-// registers otherwise.
+// z) take one row per batch without the second buffer -- both would not fit
+// in registers otherwise; (c) the residual form at 6144 keeps a 4-row burst,
+// measured faster there than the plain form's pipelined single row.
 template <int H, int FORM>
 struct BwdShape {
   static constexpr bool kWide = FORM != kPlain && Geo<H>::V > 1;
   static constexpr bool kGateBurst = FORM == kGate && !Geo<H>::PIPE;
   static constexpr int D = (kWide || kGateBurst) ? 1 : Geo<H>::D;
   static constexpr bool PIPE = kWide ? false : (kGateBurst ? true : Geo<H>::PIPE);
+};
+template <>
+struct BwdShape<6144, kResidual> {
+  static constexpr int D = 4;
+  static constexpr bool PIPE = false;
 };
 
 // Backward main kernel. Workgroup-strided over the chunks of the dw tree. The
