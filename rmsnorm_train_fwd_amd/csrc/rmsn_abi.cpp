@@ -35,10 +35,6 @@ int rows_per_subchain_group(int64_t width) {  // R: row groups per workgroup
   return bwd_rows_per_rowtask((int)width);
 }
 
-// Chunks of the dw tree for a large row count: one per workgroup of the main
-// kernel that a 256-CU part holds at once (one per CU at every width), so all
-// chunks run in one round with no tail.
-constexpr int64_t kMaxChunks = 256;
 
 struct Span {
   uintptr_t lo = 0, hi = 0;  // [lo, hi); empty if lo == hi
@@ -114,7 +110,9 @@ void make_plan(const rmsn_layout& L, int /*det*/, const rmsn_launch* o, rmsn_bwd
   // The dw tree: depends on the row count and the width only. Tiles of R
   // rows are dealt to the chunks in turn. Small row counts: at most 8 tiles
   // per chunk (one load round trip per sub-chain on the single-launch path);
-  // otherwise kMaxChunks chunks, or one per tile if there are fewer.
+  // otherwise kMaxChunks chunks (one per workgroup of the main kernel that a
+  // 256-CU part holds at once, so all chunks run in one round with no tail),
+  // or one per tile if there are fewer.
   const int64_t R = rows_per_subchain_group(L.width);
   const int64_t tiles = cdiv(rows, R);
   int64_t K = rows <= kSmallTreeRows ? cdiv(tiles, kSmallTreeTiles) : kMaxChunks;

@@ -5,44 +5,41 @@
 namespace rmsn {
 
 // One workgroup of kFoldThreads threads covers kFoldTile columns: thread
-// (g, c) sums group g of column c (its kFoldGroup chunk partials are loaded
-// first, then added in ascending order from 0.0), the group sums meet in LDS,
-// and one thread per column adds them in ascending group order from 0.0.
-// With one thread per (column, group) every partial of the call is in flight
-// at once.
+// (g, c) sums group g of column c -- its kFoldGroup chunk partials are all
+// loaded first, then added in ascending order from 0.0 -- the group sums meet
+// in LDS, and one thread per column adds them in ascending group order from
+// 0.0. The host plans at most kMaxChunks chunks, i.e. kFoldGroups groups, so
+// one pass holds every group; more would take further passes in order.
 __global__ __launch_bounds__(kFoldThreads) void k_fold(const double* __restrict__ ws,
                                                        float* __restrict__ dw, int H,
                                                        int64_t chunks) {
-  constexpr int kGroups = kFoldThreads / kFoldTile;  // 32 = max groups (<= 1024 chunks)
-  __shared__ double gsum[kGroups][kFoldTile];
+  __shared__ double gsum[kFoldGroups][kFoldTile];
   const int c = threadIdx.x % kFoldTile, g = threadIdx.x / kFoldTile;
   const int64_t groups = (chunks + kFoldGroup - 1) / kFoldGroup;
   for (int tile = blockIdx.x; tile < H / kFoldTile; tile += gridDim.x) {
     const int col = tile * kFoldTile + c;
-    if (g < groups) {
-      const int64_t k0 = (int64_t)g * kFoldGroup;
-      const int n = (int)(chunks - k0 < kFoldGroup ? chunks - k0 : kFoldGroup);
-      const double* p = ws + k0 * H + col;
-      double s = 0.0;
-      constexpr int kBatch = 16;  // loads in flight per thread
+    double t = 0.0;
+    for (int64_t g0 = 0; g0 < groups; g0 += kFoldGroups) {
+      if (g0 + g < groups) {
+        const int64_t k0 = (g0 + g) * kFoldGroup;
+        const int n = (int)(chunks - k0 < kFoldGroup ? chunks - k0 : kFoldGroup);
+        const double* p = ws + k0 * H + col;
+        double v[kFoldGroup];
 #pragma unroll
-      for (int i0 = 0; i0 < kFoldGroup; i0 += kBatch) {
-        double v[kBatch];
+        for (int i = 0; i < kFoldGroup; ++i) v[i] = i < n ? p[(int64_t)i * H] : 0.0;
+        double s = 0.0;
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) v[i] = i0 + i < n ? p[(int64_t)(i0 + i) * H] : 0.0;
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i)
-          if (i0 + i < n) s = s + v[i];
+        for (int i = 0; i < kFoldGroup; ++i)
+          if (i < n) s = s + v[i];
+        gsum[g][c] = s;
       }
-      gsum[g][c] = s;
+      __syncthreads();
+      if (g == 0) {
+        for (int j = 0; j < kFoldGroups && g0 + j < groups; ++j) t = t + gsum[j][c];
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    if (g == 0) {
-      double t = 0.0;
-      for (int64_t gg = 0; gg < groups; ++gg) t = t + gsum[gg][c];
-      dw[col] = (float)t;
-    }
-    __syncthreads();
+    if (g == 0) dw[col] = (float)t;
   }
 }
 

@@ -56,8 +56,10 @@ int fwd_rows_per_tile(int H, int form);  // rows one workgroup handles per tile
 int bwd_rows_per_rowtask(int H);   // R: row groups of the main kernel = rows per tile = sub-chains per chunk
 int small_rows_per_rowtask(int H); // rows one small-path row workgroup handles
 int small_col_tile(int H);         // columns per small-path column-task workgroup
+constexpr int kMaxChunks = 256;    // chunks of the dw tree at most (one per CU at large T)
 constexpr int kFoldGroup = 32;     // chunks per first-level group of the dw fold
+constexpr int kFoldGroups = kMaxChunks / kFoldGroup;  // first-level groups at most
 constexpr int kFoldTile = 32;      // columns per fold workgroup
-constexpr int kFoldThreads = 1024; // fold workgroup size (one thread per column x group)
+constexpr int kFoldThreads = kFoldTile * kFoldGroups; // one thread per column x group
 
 }  // namespace rmsn
