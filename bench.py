@@ -252,6 +252,12 @@ def sweep(out_path, reps=20):
                 R.rmsnorm_silu_gate_train_bwd(dy, x, z, r2, w, det, workspace=ws)
             add("5", shape, f"step 2xfwd+bwd {'det' if det else 'nondet'}", graph_time(step),
                 2 * fb + bb)
+    # next, rank 1: per-head views of width 256 at large row counts
+    for T in (4096, 16384, 65536):
+        for heads, rs, hs in ((24, 12288, 512), (24, 6144, 256), (4, 1024, 256)):
+            run_plain("n1", T, 256, "f32", [False, True], heads=heads, rs=rs, hs=hs,
+                      label=f"[{T},{heads},256] strides ({rs},{hs},1)")
+            torch.cuda.empty_cache()
     with open(out_path, "w") as fh:
         fh.write("| cfg | workload | op | us/call | algorithmic GB/s | % of 8 TB/s |\n|---|---|---|---|---|---|\n")
         for cfg, shape, op, us, gbps in rows:

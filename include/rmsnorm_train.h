@@ -134,7 +134,7 @@ rmsn_status rmsnorm_train_fwd(const void* x, const void* residual, const void* w
                               void* h_out, float* rstd, void* stream);
 
 /* ---------------------------------------------------------------- backward --
- * dx (BF16) and dw (FP32) from dy (BF16, g strides), x (BF16, x strides; the
+ * dx (BF16) and dw (FP32 or BF16) from dy (BF16, g strides), x (BF16, x strides; the
  * BF16 h of the forward in the residual form), the forward's rstd and w.
  * dh != NULL selects the residual form: the row output is grad_h = dh + dx
  * (one rounding), dh in the g strides ([C] "Residual rows").
@@ -147,17 +147,21 @@ rmsn_status rmsnorm_train_fwd(const void* x, const void* residual, const void* w
  *   (dy*x is exact in FP32, times rstd by an FMA-based TwoProduct) and
  *   TwoSum-compensated FP32 accumulation; the R sub-chains merge in order in
  *   FP64; chunk partials fold in FP64 in a fixed two-level order (groups of
- *   32 consecutive chunks, then the groups); one rounding to FP32. The result
+ *   32 consecutive chunks, then the groups); one rounding to dw_dtype. The result
  *   is bit-identical for every grid, every path and every device.
  * deterministic == 0 ([D]): same chunks and sub-chains, FP32 block sums of
  *   dy*xhat over 8 rows of a sub-chain flushed into a TwoSum-compensated
  *   pair, FP64 combine. No bitwise guarantee is made for this mode.
+ * dw_dtype: RMSN_F32, or RMSN_BF16 for dw in the weight's 16-bit format ([E]
+ *   times the gated step both ways; its stepg_f32 is the one with FP32 dw).
+ *   In both modes the FP64 value is rounded once, straight to dw_dtype.
  * workspace: at least the bytes rmsnorm_train_bwd_query reports (0 on the
  *   small path; may then be NULL). Its contents on entry do not matter.     */
 rmsn_status rmsnorm_train_bwd(const void* dy, const void* x, const void* dh, const void* w,
                               rmsn_dtype w_dtype, const float* rstd, int deterministic,
-                              const rmsn_layout* L, void* dx, float* dw, void* workspace,
-                              size_t workspace_bytes, const rmsn_launch* launch, void* stream);
+                              const rmsn_layout* L, void* dx, void* dw, rmsn_dtype dw_dtype,
+                              void* workspace, size_t workspace_bytes, const rmsn_launch* launch,
+                              void* stream);
 
 /* Host-only: the plan (path, chunking, grids, workspace bytes) of a backward
  * call with this layout, mode and override. Validates L and the override.   */
@@ -171,15 +175,15 @@ rmsn_status rmsnorm_silu_gate_train_fwd(const void* x, const void* z, const void
                                         rmsn_dtype w_dtype, float eps, const rmsn_layout* L,
                                         void* y, float* rstd, void* stream);
 
-/* Backward ([E]): dx, dz (BF16) and dw (FP32) from dy (g strides), x, z
- * (x strides), the forward's rstd and w. Modes and workspace as in
+/* Backward ([E]): dx, dz (BF16) and dw (dw_dtype) from dy (g strides), x, z
+ * (x strides), the forward's rstd and w. Modes, dw_dtype and workspace as in
  * rmsnorm_train_bwd (the query is shared). In the deterministic mode the
  * per-row term is TwoProduct(dy*x, RN(rstd*silu(z))): one rounding inside it.
  */
 rmsn_status rmsnorm_silu_gate_train_bwd(const void* dy, const void* x, const void* z,
                                         const void* w, rmsn_dtype w_dtype, const float* rstd,
                                         int deterministic, const rmsn_layout* L, void* dx,
-                                        void* dz, float* dw, void* workspace,
+                                        void* dz, void* dw, rmsn_dtype dw_dtype, void* workspace,
                                         size_t workspace_bytes, const rmsn_launch* launch,
                                         void* stream);
 

@@ -75,12 +75,12 @@ def lib():
         L = C.CDLL(LIB_PATH)
         vp, lp, lap, fp = C.c_void_p, C.POINTER(Layout), C.POINTER(Launch), C.c_float
         L.rmsnorm_train_fwd.argtypes = [vp, vp, vp, C.c_int, fp, lp, vp, vp, vp, vp]
-        L.rmsnorm_train_bwd.argtypes = [vp, vp, vp, vp, C.c_int, vp, C.c_int, lp, vp, vp, vp,
-                                        C.c_size_t, lap, vp]
+        L.rmsnorm_train_bwd.argtypes = [vp, vp, vp, vp, C.c_int, vp, C.c_int, lp, vp, vp, C.c_int,
+                                        vp, C.c_size_t, lap, vp]
         L.rmsnorm_train_bwd_query.argtypes = [lp, C.c_int, lap, C.POINTER(BwdPlan)]
         L.rmsnorm_silu_gate_train_fwd.argtypes = [vp, vp, vp, C.c_int, fp, lp, vp, vp, vp]
         L.rmsnorm_silu_gate_train_bwd.argtypes = [vp, vp, vp, vp, C.c_int, vp, C.c_int, lp, vp,
-                                                  vp, vp, vp, C.c_size_t, lap, vp]
+                                                  vp, vp, C.c_int, vp, C.c_size_t, lap, vp]
         for name in EXPORTS[:-1]:
             getattr(L, name).restype = C.c_int
         L.rmsn_status_str.argtypes = [C.c_int]
@@ -197,11 +197,21 @@ def _workspace(plan: BwdPlan, x: torch.Tensor, workspace: Optional[torch.Tensor]
     return workspace, workspace.numel() * workspace.element_size()
 
 
+def _dw(width: int, dtype: torch.dtype, device):
+    """The dw output tensor and its ABI dtype code."""
+    if dtype == torch.float32:
+        return torch.empty(width, dtype=torch.float32, device=device), RMSN_F32
+    if dtype == torch.bfloat16:
+        return torch.empty(width, dtype=torch.bfloat16, device=device), RMSN_BF16
+    raise ValueError("dw_dtype must be torch.float32 or torch.bfloat16")
+
+
 def rmsnorm_train_bwd(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor, w: torch.Tensor,
                       deterministic: bool = True, dh: Optional[torch.Tensor] = None,
-                      launch: Optional[Launch] = None, workspace: Optional[torch.Tensor] = None):
-    """dx (BF16) and dw (FP32). With dh (residual form; x is then the forward's
-    BF16 h): grad_h = dh + dx replaces dx."""
+                      launch: Optional[Launch] = None, workspace: Optional[torch.Tensor] = None,
+                      dw_dtype: torch.dtype = torch.float32):
+    """dx (BF16) and dw (FP32, or BF16 with dw_dtype=torch.bfloat16). With dh
+    (residual form; x is then the forward's BF16 h): grad_h = dh + dx replaces dx."""
     for t, n in ((dy, "dy"), (x, "x"), (rstd, "rstd")):
         _device(t, n)
     _inner_contiguous(x, "x")
@@ -216,9 +226,9 @@ def rmsnorm_train_bwd(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor, w: 
     ws, ws_bytes = _workspace(plan, x, workspace)
     full, _ = _rows_shape(x)
     dx = torch.empty(full, dtype=torch.bfloat16, device=x.device)
-    dw = torch.empty(L.width, dtype=torch.float32, device=x.device)
+    dw, dwd = _dw(L.width, dw_dtype, x.device)
     _check(lib().rmsnorm_train_bwd(_ptr(dy), _ptr(x), _ptr(dh), _ptr(w), wd, _ptr(rstd),
-                                   int(bool(deterministic)), C.byref(L), _ptr(dx), _ptr(dw),
+                                   int(bool(deterministic)), C.byref(L), _ptr(dx), _ptr(dw), dwd,
                                    _ptr(ws), ws_bytes, C.byref(launch) if launch else None,
                                    _stream(x)), "rmsnorm_train_bwd")
     return dx, dw
@@ -244,8 +254,10 @@ def rmsnorm_silu_gate_train_fwd(x: torch.Tensor, z: torch.Tensor, w: torch.Tenso
 def rmsnorm_silu_gate_train_bwd(dy: torch.Tensor, x: torch.Tensor, z: torch.Tensor,
                                 rstd: torch.Tensor, w: torch.Tensor, deterministic: bool = True,
                                 launch: Optional[Launch] = None,
-                                workspace: Optional[torch.Tensor] = None):
-    """dx, dz (BF16) and dw (FP32) of the SiLU-gated form."""
+                                workspace: Optional[torch.Tensor] = None,
+                                dw_dtype: torch.dtype = torch.float32):
+    """dx, dz (BF16) and dw (FP32, or BF16 with dw_dtype=torch.bfloat16) of the
+    SiLU-gated form."""
     for t, n in ((dy, "dy"), (x, "x"), (z, "z"), (rstd, "rstd")):
         _device(t, n)
     _inner_contiguous(x, "x")
@@ -260,10 +272,10 @@ def rmsnorm_silu_gate_train_bwd(dy: torch.Tensor, x: torch.Tensor, z: torch.Tens
     full, _ = _rows_shape(x)
     dx = torch.empty(full, dtype=torch.bfloat16, device=x.device)
     dz = torch.empty(full, dtype=torch.bfloat16, device=x.device)
-    dw = torch.empty(L.width, dtype=torch.float32, device=x.device)
+    dw, dwd = _dw(L.width, dw_dtype, x.device)
     _check(lib().rmsnorm_silu_gate_train_bwd(_ptr(dy), _ptr(x), _ptr(z), _ptr(w), wd, _ptr(rstd),
                                              int(bool(deterministic)), C.byref(L), _ptr(dx),
-                                             _ptr(dz), _ptr(dw), _ptr(ws), ws_bytes,
+                                             _ptr(dz), _ptr(dw), dwd, _ptr(ws), ws_bytes,
                                              C.byref(launch) if launch else None, _stream(x)),
            "rmsnorm_silu_gate_train_bwd")
     return dx, dz, dw

@@ -148,11 +148,12 @@ RowIn row_in(const void* p, int64_t st, int64_t sh) {
 // ---------------------------------------------------------------- backward --
 rmsn_status bwd_common(int form, const void* dy, const void* x, const void* e, const void* w,
                        rmsn_dtype w_dtype, const float* rstd, int det, const rmsn_layout* L,
-                       void* dx, void* dz, float* dw, void* ws, size_t ws_bytes,
-                       const rmsn_launch* o, void* stream) {
+                       void* dx, void* dz, void* dw, rmsn_dtype dw_dtype, void* ws,
+                       size_t ws_bytes, const rmsn_launch* o, void* stream) {
   rmsn_status st = check_layout(L);
   if (st) return st;
   if (w_dtype != RMSN_BF16 && w_dtype != RMSN_F32) return RMSN_E_DTYPE;
+  if (dw_dtype != RMSN_BF16 && dw_dtype != RMSN_F32) return RMSN_E_DTYPE;
   if (det != 0 && det != 1) return RMSN_E_ARG;
   if ((st = check_launch(o))) return st;
   const int64_t rows = L->T * L->heads;
@@ -187,7 +188,7 @@ rmsn_status bwd_common(int form, const void* dy, const void* x, const void* e, c
   const Span outs[] = {
       dense_span(dx, rbytes),
       form == kGate ? dense_span(dz, rbytes) : Span{},
-      dense_span(dw, W * 4),
+      dense_span(dw, W * (dw_dtype == RMSN_F32 ? 4 : 2)),
       dense_span(ws, (int64_t)plan.workspace_bytes),
   };
   for (const Span& a : outs) {
@@ -206,6 +207,7 @@ rmsn_status bwd_common(int form, const void* dy, const void* x, const void* e, c
   a.dx = static_cast<uint16_t*>(dx);
   a.dz = static_cast<uint16_t*>(dz);
   a.dw = dw;
+  a.dw_bf16 = dw_dtype == RMSN_BF16;
   a.ws = static_cast<double*>(ws);
   a.rows = rows;
   a.chunks = plan.chunks;
@@ -321,19 +323,20 @@ RMSN_API rmsn_status rmsnorm_silu_gate_train_fwd(const void* x, const void* z, c
 RMSN_API rmsn_status rmsnorm_train_bwd(const void* dy, const void* x, const void* dh,
                                        const void* w, rmsn_dtype w_dtype, const float* rstd,
                                        int deterministic, const rmsn_layout* L, void* dx,
-                                       float* dw, void* workspace, size_t workspace_bytes,
-                                       const rmsn_launch* launch, void* stream) {
+                                       void* dw, rmsn_dtype dw_dtype, void* workspace,
+                                       size_t workspace_bytes, const rmsn_launch* launch,
+                                       void* stream) {
   return bwd_common(dh ? kResidual : kPlain, dy, x, dh, w, w_dtype, rstd, deterministic, L, dx,
-                    nullptr, dw, workspace, workspace_bytes, launch, stream);
+                    nullptr, dw, dw_dtype, workspace, workspace_bytes, launch, stream);
 }
 
 RMSN_API rmsn_status rmsnorm_silu_gate_train_bwd(const void* dy, const void* x, const void* z,
                                                  const void* w, rmsn_dtype w_dtype,
                                                  const float* rstd, int deterministic,
                                                  const rmsn_layout* L, void* dx, void* dz,
-                                                 float* dw, void* workspace,
+                                                 void* dw, rmsn_dtype dw_dtype, void* workspace,
                                                  size_t workspace_bytes,
                                                  const rmsn_launch* launch, void* stream) {
-  return bwd_common(kGate, dy, x, z, w, w_dtype, rstd, deterministic, L, dx, dz, dw, workspace,
-                    workspace_bytes, launch, stream);
+  return bwd_common(kGate, dy, x, z, w, w_dtype, rstd, deterministic, L, dx, dz, dw, dw_dtype,
+                    workspace, workspace_bytes, launch, stream);
 }

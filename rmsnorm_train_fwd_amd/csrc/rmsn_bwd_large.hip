@@ -11,7 +11,7 @@ namespace rmsn {
 // 0.0. The host plans at most kMaxChunks chunks, i.e. kFoldGroups groups, so
 // one pass holds every group; more would take further passes in order.
 __global__ __launch_bounds__(kFoldThreads) void k_fold(const double* __restrict__ ws,
-                                                       float* __restrict__ dw, int H,
+                                                       void* __restrict__ dw, int dw_bf16, int H,
                                                        int64_t chunks) {
   __shared__ double gsum[kFoldGroups][kFoldTile];
   const int c = threadIdx.x % kFoldTile, g = threadIdx.x / kFoldTile;
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kFoldThreads) void k_fold(const double* __restrict_
       }
       __syncthreads();
     }
-    if (g == 0) dw[col] = (float)t;
+    if (g == 0) store_dw(dw, dw_bf16, col, t);
   }
 }
 
@@ -83,7 +83,7 @@ hipError_t launch_bwd_large(int H, bool w_f32, int form, bool det, const BwdArgs
 }
 
 hipError_t launch_fold(int H, const BwdArgs& a, int grid, hipStream_t s) {
-  k_fold<<<grid, kFoldThreads, 0, s>>>(a.ws, a.dw, H, a.chunks);
+  k_fold<<<grid, kFoldThreads, 0, s>>>(a.ws, a.dw, a.dw_bf16, H, a.chunks);
   return hipGetLastError();
 }
 

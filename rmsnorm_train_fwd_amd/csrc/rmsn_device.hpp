@@ -48,6 +48,20 @@ __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
   return u;
 }
 
+// FP64 -> BF16 rounded once to nearest even. The FP64 value is first rounded
+// to odd at FP32 precision (toward zero, last bit set when inexact), then
+// rounded to nearest even into BF16; rounding to odd at 24 bits followed by
+// rounding to 8 bits equals rounding the FP64 value once (Boldo and
+// Melquiond, "Emulation of FMA and correctly rounded sums: proved algorithms
+// using rounding to odd", 2008). BF16 shares FP32's exponent range.
+__device__ __forceinline__ u16 f64_to_bf16(double d) {
+  const float f = (float)d;                            // nearest even
+  u32 b = __float_as_uint(f);
+  if (__builtin_fabs((double)f) > __builtin_fabs(d)) b -= 1;  // one step toward zero
+  if ((double)__uint_as_float(b) != d) b |= 1u;        // inexact: odd
+  return (u16)(pack_bf16x2(__uint_as_float(b), 0.0f) & 0xffffu);
+}
+
 __device__ __forceinline__ uint4 ld16(const u16* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // Streaming loads/stores: data touched exactly once per call.

@@ -409,11 +409,17 @@ __global__ __launch_bounds__(Geo<H>::BLOCK) void k_bwd_large(BwdArgs a) {
   }
 }
 
-// Fold: dw[j] = RN_fp32( sum_g ( sum_{k in group g} ws[k][j] ) ), both sums in
-// ascending order from 0.0, groups of kFoldGroup consecutive chunks (defined
-// in rmsn_bwd_large.hip).
+// dw[j] from its FP64 value, rounded once to the output dtype.
+__device__ __forceinline__ void store_dw(void* dw, int bf16, int j, double v) {
+  if (bf16) static_cast<u16*>(dw)[j] = f64_to_bf16(v);
+  else static_cast<float*>(dw)[j] = (float)v;
+}
+
+// Fold: dw[j] = RN( sum_g ( sum_{k in group g} ws[k][j] ) ), both sums in
+// ascending order from 0.0, groups of kFoldGroup consecutive chunks, one
+// rounding to FP32 or BF16 (defined in rmsn_bwd_large.hip).
 __global__ __launch_bounds__(kFoldThreads) void k_fold(const double* __restrict__ ws,
-                                                       float* __restrict__ dw, int H,
+                                                       void* __restrict__ dw, int dw_bf16, int H,
                                                        int64_t chunks);
 
 // Small-row backward in one launch. Workgroups [0, row_grid) are row tasks
@@ -543,7 +549,7 @@ __global__ __launch_bounds__(SmallGeo<H>::BLOCK) void k_bwd_small(BwdArgs a, int
       }
       __syncthreads();
     }
-    if (q == 0 && kl < 8) a.dw[c0 + kl] = (float)total;
+    if (q == 0 && kl < 8) store_dw(a.dw, a.dw_bf16, c0 + kl, total);
   }
 }
 

@@ -35,7 +35,8 @@ struct BwdArgs {
   const float* rstd;  // [rows]
   uint16_t* dx;       // dense [rows, H] (grad_h in the residual form)
   uint16_t* dz;       // dense [rows, H] (kGate)
-  float* dw;          // [H]
+  void* dw;           // [H], FP32 or (dw_bf16) BF16
+  int32_t dw_bf16;
   double* ws;         // [chunks, H] FP64 chunk partials (large path)
   int64_t rows;
   int64_t chunks;     // K: chunks of the dw tree, 1 <= K <= ceil(rows / R) when rows > 0

@@ -89,3 +89,43 @@ def test_det_dw_large_path_within_one_ulp_of_exact_sum(T, H, family):
     got = _gpu_det_dw(p, r32, R.PATH_LARGE)
     gap = _ulp_gap(got, exact.astype(np.float32))
     assert gap.max() <= 1, f"det dw is {gap.max()} FP32 ulp from the exact sum"
+
+
+# ---------------------------------------------------------- dw in BF16 --
+# With dw_dtype BF16 the FP64 value is rounded once, straight to BF16.
+
+def _bits16(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("path", [R.PATH_SMALL, R.PATH_LARGE], ids=["small", "large"])
+@pytest.mark.parametrize("H", [512, 4096, 6144])
+def test_det_bf16_dw_single_row_is_the_exact_term_rounded_once(H, path):
+    p = synth.make(1, H, seed=24, w_dtype="bf16")
+    r32 = _host_rstd(p)
+    want = oracle.f64_to_bf16(_terms(p, r32)[0])
+    g = OnGpu(p)
+    r = torch.from_numpy(np.ascontiguousarray(r32)).cuda()
+    _, dw = R.rmsnorm_train_bwd(g.dy, g.x, r, g.w, True, launch=R.Launch(0, 0, path),
+                                dw_dtype=torch.bfloat16)
+    assert dw.dtype == torch.bfloat16
+    assert np.array_equal(_bits16(dw), want)
+
+
+@pytest.mark.parametrize("path", [R.PATH_SMALL, R.PATH_LARGE], ids=["small", "large"])
+@pytest.mark.parametrize("T,H,heads", [(203, 1536, 1), (203, 256, 24), (4099, 5120, 1)])
+def test_det_bf16_dw_is_the_exact_sum_rounded_once(T, H, heads, path):
+    p = synth.make(T, H, seed=25, heads=heads, w_dtype="bf16")
+    r32 = _host_rstd(p)
+    terms = _terms(p, r32)
+    exact = np.array([math.fsum(terms[:, j]) for j in range(H)])
+    g = OnGpu(p)
+    r = torch.from_numpy(np.ascontiguousarray(r32)).cuda()
+    _, dw = R.rmsnorm_train_bwd(g.dy, g.x, r, g.w, True, launch=R.Launch(0, 0, path),
+                                dw_dtype=torch.bfloat16)
+    # the FP64 fold is within ~1e-15 relative of the exact sum, so one rounding
+    # of either to BF16 agrees except at a rounding boundary: allow one ulp
+    from helpers import bf16_ulp_distance
+    gap = bf16_ulp_distance(_bits16(dw), oracle.f64_to_bf16(exact))
+    assert gap.max() <= 1
+    assert (gap == 0).mean() > 0.99

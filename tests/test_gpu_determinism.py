@@ -102,3 +102,25 @@ def test_plan_is_grid_independent():
     a = R.rmsnorm_train_bwd_query(x, True)
     b = R.rmsnorm_train_bwd_query(x, True, R.Launch(7, 3, R.PATH_LARGE))
     assert (a.chunks, a.subchains) == (b.chunks, b.subchains)
+
+
+@pytest.mark.parametrize("T,W,form", [(203, 512, "plain"), (4099, 4096, "plain"), (300, 4096, "gate")])
+def test_det_bf16_dw_bitwise_across_grids_and_paths(T, W, form):
+    p = synth.make(T, W, seed=13, w_dtype="bf16", form=form)
+    g = OnGpu(p)
+    if form == "gate":
+        _, rstd = R.rmsnorm_silu_gate_train_fwd(g.x, g.e, g.w)
+    else:
+        _, rstd = R.rmsnorm_train_fwd(g.x, g.w)
+    first = None
+    for launch in LAUNCHES:
+        if form == "gate":
+            dw = R.rmsnorm_silu_gate_train_bwd(g.dy, g.x, g.e, rstd, g.w, True, launch=launch,
+                                               dw_dtype=torch.bfloat16)[2]
+        else:
+            dw = R.rmsnorm_train_bwd(g.dy, g.x, rstd, g.w, True, launch=launch,
+                                     dw_dtype=torch.bfloat16)[1]
+        b = bits(dw)
+        if first is None:
+            first = b
+        assert np.array_equal(b, first), f"BF16 det dw bits changed with launch {launch}"

@@ -223,3 +223,36 @@ def test_zero_and_constant_rows():
     assert abs(rstd[0].item() - 1000.0) <= 1000.0 * 1e-6
     assert abs(rstd[2].item() - 1.0 / np.sqrt(9.0 + 1e-6)) <= 1e-6
     assert out["dw"] <= 1.0
+
+
+# ------------------------------------------------------- dw in BF16 --
+
+@pytest.mark.parametrize("det", [True, False], ids=["det", "nondet"])
+@pytest.mark.parametrize("T,H,form", [(8, 512, "plain"), (4099, 4096, "plain"), (65537, 2048, "plain"),
+                                      (777, 6144, "residual"), (3534, 4096, "gate")])
+def test_bf16_dw_within_one_ulp_of_the_oracle(T, H, form, det):
+    """dw_dtype BF16: the FP64 value rounded once to BF16; within one BF16 ulp
+    of the FP64 oracle rounded to BF16 (one ulp covers the FP32 blocks of the
+    non-deterministic mode and values at a rounding boundary)."""
+    p = synth.make(T, H, seed=6, w_dtype="bf16", form=form)
+    g = OnGpu(p)
+    w = w_f64(p.w)
+    if form == "residual":
+        _, rstd, h = R.rmsnorm_train_fwd(g.x, g.w, p.eps, residual=g.e)
+        _, dw = R.rmsnorm_train_bwd(g.dy, h, rstd, g.w, det, dh=g.dh, dw_dtype=torch.bfloat16)
+        ho, _, _ = oracle.res_fwd(oview(p, p.x), oview(p, p.extra), w, p.eps)
+        hb = oracle.View(ho, p.T, p.heads, H, p.heads * H, H)   # the oracle's own h
+        _, ref = oracle.bwd(oview(p, p.dy), hb, w, p.eps, dh=oview(p, p.dh), want_rows=False)
+    elif form == "gate":
+        _, rstd = R.rmsnorm_silu_gate_train_fwd(g.x, g.e, g.w, p.eps)
+        _, _, dw = R.rmsnorm_silu_gate_train_bwd(g.dy, g.x, g.e, rstd, g.w, det,
+                                                 dw_dtype=torch.bfloat16)
+        _, _, ref = oracle.gate_bwd(oview(p, p.dy), oview(p, p.x), oview(p, p.extra), w, p.eps,
+                                    want_rows=False)
+    else:
+        _, rstd = R.rmsnorm_train_fwd(g.x, g.w, p.eps)
+        _, dw = R.rmsnorm_train_bwd(g.dy, g.x, rstd, g.w, det, dw_dtype=torch.bfloat16)
+        _, ref = oracle.bwd(oview(p, p.dy), oview(p, p.x), w, p.eps, want_rows=False)
+    assert dw.dtype == torch.bfloat16
+    ulp = bf16_ulp_distance(bits(dw), oracle.f64_to_bf16(ref))
+    assert ulp.max() <= 1, f"BF16 dw differs from the rounded oracle by {ulp.max()} ulp"
