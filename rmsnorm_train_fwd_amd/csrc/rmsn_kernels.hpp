@@ -2,7 +2,7 @@
 //
 //   k_fwd        forward: y, rstd (+ h for the fused residual, silu gate)
 //   k_bwd_large  backward main kernel: dx (+dz) and FP64 dw chunk partials
-//   k_fold       fixed-order FP64 fold of the chunk partials -> dw (FP32)
+//   k_fold       fixed-order FP64 fold of the chunk partials -> dw (FP32 or BF16)
 //   k_bwd_small  single-launch backward for small row counts: row tasks for
 //                dx, column tasks for dw over all rows, no workspace
 //
@@ -21,7 +21,6 @@ __device__ __forceinline__ int64_t row_off(const RowIn& in, int64_t row, int hea
   const uint32_t h = (uint32_t)row - t * (uint32_t)heads;
   return (int64_t)t * in.stride_t + (int64_t)h * in.stride_h;
 }
-
 
 // Forward shape per width and form: the backward's, except the gated form at
 // 5120, which keeps one 640-thread row group (8 columns per thread) where the
@@ -118,11 +117,10 @@ __global__ __launch_bounds__((FGeo<H, FORM>::BLOCK)) void k_fwd(FwdArgs a) {
 
 // ----------------------------------------------------------------- backward --
 //
-// One batch of D rows of one row group: loads, the row sum c = sum g*xhat,
-// dx = rstd*(g - xhat*c/H) (+dh), dz for the gate, stores. Returns the loaded
-// x, dy (and z) for the dw accumulation. The arithmetic of a row does not
-// depend on D or on the kernel calling it, so dx has the same bits on every
-// path.
+// One batch of D rows of one row group: loads, the rows' dw terms into the
+// caller's accumulators, the row sum c = sum g*xhat, dx = rstd*(g - xhat*c/H)
+// (+dh), dz for the gate, stores. The arithmetic of a row does not depend on
+// D or on the kernel calling it, so dx has the same bits on every path.
 struct NoDw {};  // accumulator policy of row tasks that only write dx
 
 template <int H, int FORM, int D>
@@ -260,19 +258,17 @@ struct RowBatch {
   }
 };
 
-// Batch shape of the backward main kernel for one form: the width's default,
-// except that (a) the gated form (which also carries z) keeps to one row per
-// batch, pipelined, where the default is a multi-row burst; (b) with two
-// vectors per thread (V = 2) the residual and gated forms (which carry dh or
-// z) take one row per batch without the second buffer -- both would not fit
-// in registers otherwise; (c) the residual form at 6144 keeps a 4-row burst,
-// measured faster there than the plain form's pipelined single row.
+// Batch shape of the backward main kernel for one form: the width's default
+// (D rows per batch, pipelined), except that (a) with two vectors per thread
+// (V = 2) the residual and gated forms, which also carry dh or z, take one row
+// per batch without the second buffer, which would not fit in registers; and
+// (b) the residual form at 6144 takes a 4-row burst, measured faster there
+// than the plain form's pipelined single row.
 template <int H, int FORM>
 struct BwdShape {
   static constexpr bool kWide = FORM != kPlain && Geo<H>::V > 1;
-  static constexpr bool kGateBurst = FORM == kGate && !Geo<H>::PIPE;
-  static constexpr int D = (kWide || kGateBurst) ? 1 : Geo<H>::D;
-  static constexpr bool PIPE = kWide ? false : (kGateBurst ? true : Geo<H>::PIPE);
+  static constexpr int D = kWide ? 1 : Geo<H>::D;
+  static constexpr bool PIPE = kWide ? false : Geo<H>::PIPE;
 };
 template <>
 struct BwdShape<6144, kResidual> {
@@ -291,7 +287,7 @@ template <int H, bool WF32, int FORM, bool DET, int D>
 __global__ __launch_bounds__(Geo<H>::BLOCK) void k_bwd_large(BwdArgs a) {
   using G = Geo<H>;
   constexpr int R = G::R, V = G::V, E = G::E, TPR = G::TPR;
-  static_assert(8 % D == 0, "a batch must not straddle an 8-row block");
+  static_assert(8 % D == 0, "a batch must not straddle a flush of the 8-row blocks");
   const int q = row_group<G>(), lane = threadIdx.x % TPR;
   __shared__ float slots[RowSum<G, D>::kSlots];
   __shared__ double merge[R > 1 ? H : 1];
@@ -403,7 +399,7 @@ __global__ __launch_bounds__(Geo<H>::BLOCK) void k_bwd_large(BwdArgs a) {
         }
         __syncthreads();
       }
-      for (int i = threadIdx.x; i < H; i += Geo<H>::BLOCK) out[i] = merge[i];
+      for (int i = threadIdx.x; i < H; i += G::BLOCK) out[i] = merge[i];
       __syncthreads();
     }
   }
