@@ -262,8 +262,9 @@ struct RowBatch {
 // (D rows per batch, pipelined), except that (a) with two vectors per thread
 // (V = 2) the residual and gated forms, which also carry dh or z, take one row
 // per batch without the second buffer, which would not fit in registers; and
-// (b) the residual form at 6144 takes a 4-row burst, measured faster there
-// than the plain form's pipelined single row.
+// (b) the residual form at 6144 takes a 2-row burst, measured faster there
+// than the plain form's pipelined single row (and than 1-, 4-row bursts or
+// 2 rows pipelined).
 template <int H, int FORM>
 struct BwdShape {
   static constexpr bool kWide = FORM != kPlain && Geo<H>::V > 1;
@@ -272,7 +273,7 @@ struct BwdShape {
 };
 template <>
 struct BwdShape<6144, kResidual> {
-  static constexpr int D = 4;
+  static constexpr int D = 2;
   static constexpr bool PIPE = false;
 };
 
