@@ -16,14 +16,28 @@ using namespace rmsn;
 
 constexpr int64_t kWidths[] = {256, 512, 1536, 2048, 4096, 5120, 6144};
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
-constexpr int64_t kSmallTreeRows = 256;  // row counts whose chunks hold at most ...
-constexpr int64_t kSmallTreeTiles = 8;   // ... this many tiles
+constexpr int64_t kSmallTreeTiles = 8;   // tiles per chunk at most, for small row counts
 constexpr int64_t kMaxStride = int64_t(1) << 40;
 constexpr int32_t kMaxGrid = 1 << 24;
 
-// Rows at or below which the backward runs as one launch (row tasks + column
-// tasks). Both paths give the same bits; this is only a speed choice.
-int64_t small_path_max_rows(int64_t /*width*/) { return 256; }
+// Small row counts, per width: at or below these, the dw tree gives each
+// chunk at most kSmallTreeTiles tiles, and the backward runs as one launch
+// (row tasks + column tasks) unless a launch override says otherwise. The
+// values are where the single launch stopped beating main kernel + fold on
+// MI355X (back-to-back calls, launch cost included); the column tasks re-read
+// x and dy over width / columns-per-task workgroups, so the crossover falls as
+// rows get wider. Both paths give the same bits.
+int64_t small_rows(int64_t width) {
+  switch (width) {
+    case 256: return 2048;
+    case 512: return 2048;
+    case 1536: return 1024;
+    case 2048: return 1024;
+    case 4096: return 768;
+    case 5120: return 512;
+    default: return 384;  // 6144
+  }
+}
 
 bool width_ok(int64_t w) {
   for (int64_t k : kWidths)
@@ -109,13 +123,15 @@ void make_plan(const rmsn_layout& L, int /*det*/, const rmsn_launch* o, rmsn_bwd
   p->rows = rows;
   // The dw tree: depends on the row count and the width only. Tiles of R
   // rows are dealt to the chunks in turn. Small row counts: at most 8 tiles
-  // per chunk (one load round trip per sub-chain on the single-launch path);
+  // per chunk (one load round trip per sub-chain on the single-launch path,
+  // and at most two 32-chunk fold groups);
   // otherwise kMaxChunks chunks (one per workgroup of the main kernel that a
   // 256-CU part holds at once, so all chunks run in one round with no tail),
   // or one per tile if there are fewer.
   const int64_t R = rows_per_subchain_group(L.width);
   const int64_t tiles = cdiv(rows, R);
-  int64_t K = rows <= kSmallTreeRows ? cdiv(tiles, kSmallTreeTiles) : kMaxChunks;
+  const bool small = rows <= small_rows(L.width);
+  int64_t K = small ? cdiv(tiles, kSmallTreeTiles) : kMaxChunks;
   if (K > tiles) K = tiles;
   p->chunks = K;
   p->subchains = (int32_t)R;
@@ -123,7 +139,7 @@ void make_plan(const rmsn_layout& L, int /*det*/, const rmsn_launch* o, rmsn_bwd
   int path = o ? o->path : RMSN_PATH_AUTO;
   if (rows == 0) path = RMSN_PATH_SMALL;  // only dw = 0 to write
   if (path == RMSN_PATH_AUTO)
-    path = rows <= small_path_max_rows(L.width) ? RMSN_PATH_SMALL : RMSN_PATH_LARGE;
+    path = small ? RMSN_PATH_SMALL : RMSN_PATH_LARGE;
   p->path = path;
   const int32_t col_tiles = (int32_t)(L.width / small_col_tile((int)L.width));
   if (path == RMSN_PATH_SMALL) {

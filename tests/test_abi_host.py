@@ -195,22 +195,26 @@ def query(T, W, heads=1, det=1, launch=None):
 
 
 SUBCHAINS = {256: 16, 512: 8, 1536: 4, 2048: 4, 4096: 2, 5120: 2, 6144: 1}
+SMALL_ROWS = {256: 2048, 512: 2048, 1536: 1024, 2048: 1024, 4096: 768, 5120: 512, 6144: 384}
 
 
-@pytest.mark.parametrize("W", [256, 512, 4096, 5120, 6144])
-@pytest.mark.parametrize("rows", [1, 15, 16, 17, 203, 256, 257, 300, 16384, 16385, 65537, 98304,
-                                  131072, 113536, 786432, 3145728])
+@pytest.mark.parametrize("W", [256, 512, 1536, 2048, 4096, 5120, 6144])
+@pytest.mark.parametrize("rows", [1, 15, 16, 17, 203, 256, 257, 300, 384, 385, 512, 513, 768, 769,
+                                  1024, 1025, 2048, 2049, 16384, 16385, 65537, 98304, 131072,
+                                  113536, 786432, 3145728])
 def test_dw_tree_chunking(rows, W):
     p = query(rows, W)
     assert p.subchains == SUBCHAINS[W] and p.fold_group == 32
     tiles = -(-rows // p.subchains)
     assert 1 <= p.chunks <= tiles          # every chunk holds at least one tile
-    if rows <= 256:
-        # as few chunks as hold at most 8 tiles each
-        assert p.chunks == -(-tiles // 8)
+    if rows <= SMALL_ROWS[W]:
+        # as few chunks as hold at most 8 tiles each; at most two fold groups
+        assert p.chunks == -(-tiles // 8) and p.chunks <= 64
+        assert p.path == R.PATH_SMALL and p.workspace_bytes == 0
     else:
         # one chunk per workgroup a 256-CU part holds at once (one per CU)
         assert p.chunks == min(tiles, 256)
+        assert p.path == R.PATH_LARGE
     # the tree depends on the row count and the width only: not on the mode,
     # the grid or the path
     for other in (query(rows, W, det=0), query(rows, W, launch=R.Launch(5, 2, R.PATH_LARGE)),
