@@ -252,6 +252,27 @@ def sweep(out_path, reps=20):
                 R.rmsnorm_silu_gate_train_bwd(dy, x, z, r2, w, det, workspace=ws)
             add("5", shape, f"step 2xfwd+bwd {'det' if det else 'nondet'}", graph_time(step),
                 2 * fb + bb)
+    # next, rank 2: the grouped per-head SiLU gate at the five tokens x heads shapes
+    # of the gated page's Table 1; head dim 256 stands in for the unstated one
+    for T, heads in ((3534, 48), (4097, 48), (6000, 48), (7684, 48), (8192, 32)):
+        W = 256
+        p = synth.make(T, W, seed=0, heads=heads, w_dtype="f32", form="gate")
+        shp = ((T, heads, W), (heads * W, W, 1))
+        x, z = p.x.to(dev).as_strided(*shp), p.extra.to(dev).as_strided(*shp)
+        dy = p.dy.to(dev).as_strided(*shp)
+        w = p.w.to(dev)
+        y, rstd = R.rmsnorm_silu_gate_train_fwd(x, z, w, p.eps)
+        rws = T * heads
+        shape = f"[{T},{heads},{W}] gate w f32"
+        fb, bb = 6 * rws * W + 4 * rws + 4 * W, 10 * rws * W + 4 * rws + 8 * W
+        add("n2", shape, "fwd", graph_time(lambda: R.rmsnorm_silu_gate_train_fwd(x, z, w, p.eps)), fb)
+        for det in (False, True):
+            plan = R.rmsnorm_train_bwd_query(x, det)
+            ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+            add("n2", shape, f"bwd {'det' if det else 'nondet'}", graph_time(
+                lambda: R.rmsnorm_silu_gate_train_bwd(dy, x, z, rstd, w, det, workspace=ws)), bb)
+        del x, z, dy, y, rstd
+        torch.cuda.empty_cache()
     # next, rank 1: per-head views of width 256 at large row counts
     for T in (4096, 16384, 65536):
         for heads, rs, hs in ((24, 12288, 512), (24, 6144, 256), (4, 1024, 256)):

@@ -256,3 +256,23 @@ def test_bf16_dw_within_one_ulp_of_the_oracle(T, H, form, det):
     assert dw.dtype == torch.bfloat16
     ulp = bf16_ulp_distance(bits(dw), oracle.f64_to_bf16(ref))
     assert ulp.max() <= 1, f"BF16 dw differs from the rounded oracle by {ulp.max()} ulp"
+
+
+# ------------------------------------------------- grouped per-head gate --
+# The PR #8656 page (Tables 1 and 2) times the gated form on tokens x heads
+# shapes: each head's slice is normalised on its own and gated by its own z, one
+# w shared by all heads. The head dimension is not stated there; these cases use
+# 256 (the per-head width of the other pages) and 512.
+
+@pytest.mark.parametrize("det", [True, False], ids=["det", "nondet"])
+@pytest.mark.parametrize("T,heads,W", [(37, 48, 256), (300, 48, 256), (40, 8, 512), (257, 8, 512)])
+def test_grouped_per_head_gate(T, heads, W, det):
+    run_case(synth.make(T, W, seed=8, heads=heads, w_dtype="f32", form="gate"), det=det,
+             form="gate")
+
+
+@pytest.mark.parametrize("det", [True, False], ids=["det", "nondet"])
+@pytest.mark.parametrize("T,heads", [(3534, 48), (8192, 32)])
+def test_grouped_per_head_gate_table_shapes(T, heads, det):
+    run_case(synth.make(T, 256, seed=9, heads=heads, w_dtype="f32", form="gate"), det=det,
+             form="gate", nsample=64)
