@@ -75,6 +75,47 @@ def time_calls(fn, steps, warmup, torch):
     return ev, wall
 
 
+def stream_ceiling(x, dy, steps, torch):
+    """The practical HBM ceiling beside the kernels: the bandwidth probe
+    (librmsn_probe.so, built with the library) streams the backward's inputs
+    in the same tile-dealt pattern with no arithmetic: two read + one written,
+    one read + one written, read only. The output is allocated here, after the
+    timed calls have freed theirs, so the caching allocator hands it the block
+    their dx and y used (the same relative placement, which matters on this
+    device). GB/s from the mean of HIP-event times."""
+    import ctypes
+
+    path = os.path.join(ROOT, "rmsnorm_train_fwd_amd", "librmsn_probe.so")
+    if not os.path.exists(path):
+        print("[bench] bandwidth probe not built; ceiling omitted", file=sys.stderr, flush=True)
+        return None
+    f = ctypes.CDLL(path).rmsn_stream_probe
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    nbytes = x.numel() * x.element_size()
+    assert dy.numel() * dy.element_size() == nbytes and x.is_contiguous() and dy.is_contiguous()
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream().cuda_stream
+    out_ = {"by_pattern": {"dealt": {}, "oneshot": {}}}
+    for nin, key, moved in ((2, "r2w1_GBps", 3 * nbytes), (1, "r1w1_GBps", 2 * nbytes),
+                            (0, "r1_GBps", nbytes)):
+        for pattern, name in ((0, "dealt"), (1, "oneshot")):
+            def call():
+                rc = f(nin, pattern, x.data_ptr(), dy.data_ptr(), out.data_ptr(), nbytes, 256,
+                       stream)
+                if rc != 0:
+                    raise RuntimeError(f"bandwidth probe failed: hip error {rc}")
+            ev, _ = time_calls(call, steps, 3, torch)
+            out_["by_pattern"][name][key] = round(moved / (sum(ev) / len(ev) * 1e-3) / 1e9, 1)
+        out_[key] = max(v[key] for v in out_["by_pattern"].values())
+    out_["probe"] = ("the backward's x and dy in 16 KiB tiles, 16-byte non-temporal accesses, no "
+                     "arithmetic; dealt: 256 workgroups x 1024 threads, tiles dealt in turn, next "
+                     "tile's loads in flight (the kernels' pattern); oneshot: one 256-thread "
+                     "workgroup per tile; the ceiling is the faster of the two")
+    return out_
+
+
 def cpu_baseline(p, rows_sample, reps=3):
     """The FP64 oracle (single-threaded C) on the workload's rows: median of reps."""
     import numpy as np
@@ -537,6 +578,8 @@ def main():
     print("[bench] timing backward (deterministic) and forward", file=sys.stderr, flush=True)
     ev_d, _ = time_calls(bwd_d, max(10, args.steps // 2), 3, torch)
     ev_f, _ = time_calls(fwd, max(10, args.steps // 2), 3, torch)
+    print("[bench] timing the bandwidth probe", file=sys.stderr, flush=True)
+    ceiling = stream_ceiling(x, dy, max(10, args.steps // 2), torch)
 
     def med(v):
         return v[len(v) // 2]
@@ -582,6 +625,8 @@ def main():
             "bwd_det_GBps": round(bwd_bytes(T_HEAD, H_HEAD, 4) / (med(ev_d) * 1e-3) / 1e9, 1),
             "fwd_us": round(med(ev_f) * 1e3, 2),
             "fwd_GBps": round(fwd_bytes(T_HEAD, H_HEAD, 4) / (med(ev_f) * 1e-3) / 1e9, 1),
+            "ceiling": ceiling,
+            "bwd_vs_r2w1_ceiling": round(gbps / ceiling["r2w1_GBps"], 4) if ceiling else None,
         },
     }
     if not args.no_cpu:

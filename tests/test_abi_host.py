@@ -233,3 +233,25 @@ def test_plan_headline_and_paths():
     assert z.path == R.PATH_SMALL and z.grid == 0 and z.workspace_bytes == 0
     forced = query(100, 2048, launch=R.Launch(0, 0, R.PATH_LARGE))
     assert forced.path == R.PATH_LARGE and forced.workspace_bytes == forced.chunks * 2048 * 8
+
+
+def test_bandwidth_probe_library_loads_and_rejects_bad_arguments():
+    # The probe that bench.py times beside the kernels (a separate library, not
+    # part of the normalisation ABI). Only argument errors are exercised here:
+    # they return before any HIP call, so nothing launches.
+    path = os.path.join(os.path.dirname(R.__file__), "librmsn_probe.so")
+    f = C.CDLL(path).rmsn_stream_probe
+    f.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int,
+                  C.c_void_p]
+    f.restype = C.c_int
+    invalid = 1  # hipErrorInvalidValue
+    a, b, o = 1 << 20, 2 << 20, 3 << 20  # 16-byte aligned stand-ins, never dereferenced
+    tile = 16 << 10
+    assert f(3, 0, a, b, o, tile, 256, None) == invalid       # nin out of range
+    assert f(2, 2, a, b, o, tile, 256, None) == invalid       # pattern out of range
+    assert f(2, 0, a, None, o, tile, 256, None) == invalid    # two inputs need b
+    assert f(1, 0, a, None, None, tile, 256, None) == invalid  # no output
+    assert f(1, 0, a, None, o, tile + 16, 256, None) == invalid  # not whole 16 KiB tiles
+    assert f(1, 0, a, None, o, 0, 256, None) == invalid       # empty
+    assert f(1, 0, a, None, o, tile, 0, None) == invalid      # no workgroups
+    assert f(1, 0, a + 8, None, o, tile, 256, None) == invalid  # misaligned
