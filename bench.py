@@ -420,10 +420,20 @@ def stats_report(stats_csv, out_md, command):
             gb = f"{bwd_bytes(T_HEAD, H_HEAD, 4) / (avg * 1e-6) / 1e9:.0f} (main kernel alone)"
         elif "k_fwd" in n:
             gb = f"{fwd_bytes(T_HEAD, H_HEAD, 4) / (avg * 1e-6) / 1e9:.0f}"
+        elif "k_stream" in n:
+            # bandwidth probe over the bench's tensors: k_stream<nin> moves (nin + 1)
+            # tensors of T*H BF16 (nin = 0: one, read only)
+            nin = int(n.split("<")[1][0])
+            moved = (nin + 1) * 2 * T_HEAD * H_HEAD
+            gb = f"{moved / (avg * 1e-6) / 1e9:.0f} (probe, {nin or 1} read{'s' if nin == 2 else ''}" \
+                 f"{', 1 written' if nin else ''})"
         lines.append(f"| `{n}` | {r['Calls']} | {avg:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {gb} |")
     lines += ["", "k_bwd_large template arguments: <width, FP32 weight, form (0 = plain), "
-              "deterministic, rows per batch>. One backward call = k_bwd_large + k_fold."]
+              "deterministic, rows per batch>. One backward call = k_bwd_large + k_fold.",
+              "k_stream / k_stream_oneshot: the bandwidth probe (librmsn_probe.so) over the same "
+              "tensors, no arithmetic: the dealt-tile pattern of the kernels and a one-shot "
+              "pattern; <nin> = tensors read (0 = read only, nothing written)."]
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
