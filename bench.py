@@ -140,7 +140,26 @@ def cpu_baseline(p, rows_sample, reps=3):
                   f"rows, width {W}, FP64 C oracle, median of {reps} runs ({dt:.2f} s each); "
                   "same algorithmic byte model as value",
         "us_per_call": round(dt * 1e6 * p.T / rows_sample, 1),
+        "host": host_cpu(),
     }
+
+
+def host_cpu():
+    """CPU model and the logical CPUs this process may run on (the oracle uses one)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count()
+    return {"model": model, "cpus_available": avail}
 
 
 def traffic_probe():
@@ -332,11 +351,12 @@ def sweep(out_path, reps=20):
     return rows
 
 
-def sweep_kernels(sweep_json, trace_dir, out_md):
-    """Kernel-active span per call from a rocprofv3 --kernel-trace --marker-trace
-    run of --sweep: per marker range (one case), the dispatches of this
-    library between two cache-flush dispatches form one replay; its span runs
-    from the first start to the last end. Median over the replays."""
+def sweep_spans(sweep_json, trace_dir):
+    """Kernel-active spans (ns) per case of one rocprofv3 --kernel-trace
+    --marker-trace run of --sweep: per marker range (one case), the dispatches
+    of this library between two cache-flush dispatches form one replay; its
+    span runs from the first start to the last end. Returns {(cfg, workload,
+    op): (spans, event_us, bytes)} in case order."""
     import csv
     import glob
 
@@ -352,22 +372,7 @@ def sweep_kernels(sweep_json, trace_dir, out_md):
         msg = r.get("Message") or r.get("Function") or ""
         if msg.startswith("rmsn_case_"):
             ranges[int(msg.split("_")[-1])] = (int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
-    out = ["# Every workload: kernel-active time per call, cold caches (rocprofv3)", "",
-           "Commands (repository root $REPO on the MI355X box; committed files only):", "", "```",
-           "cd /tmp && export TMPDIR=/tmp",
-           "rocprofv3 --kernel-trace --marker-trace --output-format csv -d $REPO/gpurun_out/prof_sweep "
-           "-o sweep -- python3 $REPO/bench.py --sweep $REPO/gpurun_out/sweep.md",
-           "python3 $REPO/bench.py --sweep-kernels $REPO/gpurun_out/sweep.md.json "
-           "$REPO/gpurun_out/prof_sweep <this file>", "```", "",
-           "Each call is one graph replay after a 512 MB read that evicts L2 and the Infinity Cache. "
-           "Kernel-active span = first kernel start to last kernel end of the call (all of this "
-           "library's kernels of the call: main + fold on the large path), median of 20 calls. "
-           "The event column is the HIP-event time around the replay, which carries a ~13 us "
-           "floor on this system (a one-element kernel measures 13.4 us that way). GB/s uses the "
-           "algorithmic bytes: fwd 4TH, bwd 6TH, residual 8TH each way, gate fwd 6TH and bwd "
-           "10TH (+ per-row and per-column terms).", "",
-           "| cfg | workload | op | kernel-active us/call | algorithmic GB/s | % of 8 TB/s | event us/call |",
-           "|---|---|---|---|---|---|---|"]
+    out = {}
     for c in cases:
         if c["case"] not in ranges or c["cfg"] == "-":
             continue
@@ -376,9 +381,7 @@ def sweep_kernels(sweep_json, trace_dir, out_md):
         for s_, e_, name in kern:
             if s_ < t0 or s_ > t1:
                 continue
-            ours = "rmsn::" in name or c["cfg"] == "-"
-            flush = not ours or ("reduce" in name and c["cfg"] == "-")
-            if flush:
+            if "rmsn::" not in name:  # the cache-flush read between replays
                 if cur:
                     spans.append(cur[1] - cur[0])
                 cur = None
@@ -386,14 +389,59 @@ def sweep_kernels(sweep_json, trace_dir, out_md):
                 cur = (s_, e_) if cur is None else (cur[0], max(cur[1], e_))
         if cur:
             spans.append(cur[1] - cur[0])
-        if not spans:
+        if spans:
+            out[(c["cfg"], c["workload"], c["op"])] = (spans, c["event_us"], c["bytes"])
+    return out
+
+
+def sweep_kernels(args, out_md):
+    """Markdown table of kernel-active time per call for every workload from
+    one or more traced --sweep runs (separate processes): median over all
+    calls of all runs, p10-p90, and each run's own median (an A/A check: the
+    same case measured again in another process)."""
+    if len(args) < 2 or len(args) % 2:
+        raise SystemExit("--sweep-kernels takes SWEEP.md.json TRACE_DIR pairs, then OUT.md")
+    runs = [sweep_spans(args[i], args[i + 1]) for i in range(0, len(args), 2)]
+    n = len(runs)
+    names = "abcdefgh"[:n]
+    pairs = " ".join(f"$REPO/gpurun_out/sweep_{k}.md.json $REPO/gpurun_out/prof_sweep_{k}"
+                     for k in names)
+    out = ["# Every workload: kernel-active time per call, cold caches (rocprofv3)", "",
+           "Commands (repository root $REPO on the MI355X box; committed files only), "
+           f"{n} separate process{'es' if n > 1 else ''}, k = {', '.join(names)}:",
+           "", "```", "cd /tmp && export TMPDIR=/tmp",
+           "rocprofv3 --kernel-trace --marker-trace --output-format csv -d $REPO/gpurun_out/prof_sweep_<k> "
+           "-o sweep -- python3 $REPO/bench.py --sweep $REPO/gpurun_out/sweep_<k>.md",
+           f"python3 $REPO/bench.py --sweep-kernels {pairs} <this file>", "```", "",
+           "Each call is one graph replay after a 512 MB read that evicts L2 and the Infinity Cache. "
+           "Kernel-active span = first kernel start to last kernel end of the call (all of this "
+           "library's kernels of the call: main + fold on the large path). The median and p10-p90 "
+           f"run over all calls of all {n} process{'es' if n > 1 else ''} (20 calls each); the "
+           "per-process medians are the A/A check (the same case measured in another process, "
+           "where the caching allocator may place the tensors elsewhere). The event column is "
+           "the HIP-event time around the replay (median of the processes), which carries a ~13 "
+           "us floor on this system. GB/s uses the algorithmic bytes and the median: fwd 4TH, bwd "
+           "6TH, residual 8TH each way, gate fwd 6TH and bwd 10TH (+ per-row and per-column "
+           "terms).", "",
+           "| cfg | workload | op | kernel-active us/call (median) | p10-p90 | per-process medians "
+           "| algorithmic GB/s | % of 8 TB/s | event us/call |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for key in runs[0]:
+        if not all(key in r for r in runs):
             continue
-        spans.sort()
-        us = spans[len(spans) // 2] / 1e3
-        gbps = c["bytes"] / (us * 1e3) if c["bytes"] else None
-        out.append(f"| {c['cfg']} | {c['workload']} | {c['op']} | {us:.2f} | "
+        allspans = sorted(x for r in runs for x in r[key][0])
+        med = allspans[len(allspans) // 2] / 1e3
+        p10 = allspans[len(allspans) // 10] / 1e3
+        p90 = allspans[(9 * len(allspans)) // 10] / 1e3
+        per = [sorted(r[key][0])[len(r[key][0]) // 2] / 1e3 for r in runs]
+        ev = sorted(r[key][1] for r in runs)[n // 2]
+        nbytes = runs[0][key][2]
+        gbps = nbytes / (med * 1e3) if nbytes else None
+        cfg, wl, op = key
+        out.append(f"| {cfg} | {wl} | {op} | {med:.2f} | {p10:.2f}-{p90:.2f} | "
+                   f"{' / '.join(f'{v:.2f}' for v in per)} | "
                    f"{f'{gbps:.0f}' if gbps else '-'} | "
-                   f"{f'{100 * gbps / HBM_PEAK_GBPS:.1f}' if gbps else '-'} | {c['event_us']:.2f} |")
+                   f"{f'{100 * gbps / HBM_PEAK_GBPS:.1f}' if gbps else '-'} | {ev:.2f} |")
     with open(out_md, "w") as fh:
         fh.write("\n".join(out) + "\n")
     print("\n".join(out))
@@ -525,7 +573,7 @@ def main():
                     help="only run the copy + backward calls that the counter runs read")
     ap.add_argument("--sweep", metavar="OUT.md",
                     help="time every workload (cold caches, graph replay) into a markdown table")
-    ap.add_argument("--sweep-kernels", nargs=3, metavar=("SWEEP.md.json", "TRACE_DIR", "OUT.md"),
+    ap.add_argument("--sweep-kernels", nargs="+", metavar="ARG",
                     help="kernel-active times of a --sweep run traced by rocprofv3")
     ap.add_argument("--stats-report", nargs=2, metavar=("KERNEL_STATS.csv", "OUT.md"))
     ap.add_argument("--traffic-report", nargs=4,
@@ -540,7 +588,7 @@ def main():
         traffic_report(*args.traffic_report)
         return
     if args.sweep_kernels:
-        sweep_kernels(*args.sweep_kernels)
+        sweep_kernels(args.sweep_kernels[:-1], args.sweep_kernels[-1])
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
