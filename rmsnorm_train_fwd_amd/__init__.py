@@ -119,6 +119,16 @@ def _device(t: torch.Tensor, name: str):
         raise RuntimeError(f"{name} must be on a ROCm GPU device (no CPU path exists)")
 
 
+def _on_device(x: torch.Tensor, **tensors):
+    """Every given tensor (None allowed) must sit on x's GPU: the kernels
+    dereference all of them on that device."""
+    _device(x, "x")
+    for name, t in tensors.items():
+        if t is not None and t.device != x.device:
+            raise ValueError(f"{name} is on {t.device}, x on {x.device}: all tensors of a call "
+                             "must be on the same GPU")
+
+
 def _layout(x: torch.Tensor, g: Optional[torch.Tensor]) -> Layout:
     gx = _geometry(x, "x")
     gg = _geometry(g, "dy") if g is not None else gx
@@ -164,7 +174,7 @@ def rmsnorm_train_fwd(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
                       residual: Optional[torch.Tensor] = None):
     """y = RMSNorm(x) * w (BF16) and rstd (FP32). With a residual: h = x + residual
     (BF16) is normalised and returned as well: (y, rstd, h)."""
-    _device(x, "x")
+    _on_device(x, w=w, residual=residual)
     _inner_contiguous(x, "x")
     L = _layout(x, None)
     wd = _w(w, L.width)
@@ -174,8 +184,10 @@ def rmsnorm_train_fwd(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
     y = torch.empty(full, dtype=torch.bfloat16, device=x.device)
     rstd = torch.empty(rows, dtype=torch.float32, device=x.device)
     h = torch.empty(full, dtype=torch.bfloat16, device=x.device) if residual is not None else None
-    _check(lib().rmsnorm_train_fwd(_ptr(x), _ptr(residual), _ptr(w), wd, float(eps), C.byref(L),
-                                   _ptr(y), _ptr(h), _ptr(rstd), _stream(x)), "rmsnorm_train_fwd")
+    with torch.cuda.device(x.device):
+        _check(lib().rmsnorm_train_fwd(_ptr(x), _ptr(residual), _ptr(w), wd, float(eps),
+                                       C.byref(L), _ptr(y), _ptr(h), _ptr(rstd), _stream(x)),
+               "rmsnorm_train_fwd")
     return (y, rstd) if h is None else (y, rstd, h)
 
 
@@ -194,6 +206,8 @@ def _workspace(plan: BwdPlan, x: torch.Tensor, workspace: Optional[torch.Tensor]
         return None, 0
     if workspace is None:
         workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=x.device)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -212,8 +226,7 @@ def rmsnorm_train_bwd(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor, w: 
                       dw_dtype: torch.dtype = torch.float32):
     """dx (BF16) and dw (FP32, or BF16 with dw_dtype=torch.bfloat16). With dh
     (residual form; x is then the forward's BF16 h): grad_h = dh + dx replaces dx."""
-    for t, n in ((dy, "dy"), (x, "x"), (rstd, "rstd")):
-        _device(t, n)
+    _on_device(x, dy=dy, rstd=rstd, w=w, dh=dh, workspace=workspace)
     _inner_contiguous(x, "x")
     _inner_contiguous(dy, "dy")
     L = _layout(x, dy)
@@ -227,17 +240,19 @@ def rmsnorm_train_bwd(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor, w: 
     full, _ = _rows_shape(x)
     dx = torch.empty(full, dtype=torch.bfloat16, device=x.device)
     dw, dwd = _dw(L.width, dw_dtype, x.device)
-    _check(lib().rmsnorm_train_bwd(_ptr(dy), _ptr(x), _ptr(dh), _ptr(w), wd, _ptr(rstd),
-                                   int(bool(deterministic)), C.byref(L), _ptr(dx), _ptr(dw), dwd,
-                                   _ptr(ws), ws_bytes, C.byref(launch) if launch else None,
-                                   _stream(x)), "rmsnorm_train_bwd")
+    with torch.cuda.device(x.device):
+        _check(lib().rmsnorm_train_bwd(_ptr(dy), _ptr(x), _ptr(dh), _ptr(w), wd, _ptr(rstd),
+                                       int(bool(deterministic)), C.byref(L), _ptr(dx), _ptr(dw),
+                                       dwd, _ptr(ws), ws_bytes,
+                                       C.byref(launch) if launch else None, _stream(x)),
+               "rmsnorm_train_bwd")
     return dx, dw
 
 
 def rmsnorm_silu_gate_train_fwd(x: torch.Tensor, z: torch.Tensor, w: torch.Tensor,
                                 eps: float = 1e-6):
     """y = RMSNorm(x) * w * silu(z) (BF16) and rstd (FP32)."""
-    _device(x, "x")
+    _on_device(x, z=z, w=w)
     _inner_contiguous(x, "x")
     _same_geometry(x, z, "x", "z")
     L = _layout(x, None)
@@ -245,9 +260,10 @@ def rmsnorm_silu_gate_train_fwd(x: torch.Tensor, z: torch.Tensor, w: torch.Tenso
     full, rows = _rows_shape(x)
     y = torch.empty(full, dtype=torch.bfloat16, device=x.device)
     rstd = torch.empty(rows, dtype=torch.float32, device=x.device)
-    _check(lib().rmsnorm_silu_gate_train_fwd(_ptr(x), _ptr(z), _ptr(w), wd, float(eps), C.byref(L),
-                                             _ptr(y), _ptr(rstd), _stream(x)),
-           "rmsnorm_silu_gate_train_fwd")
+    with torch.cuda.device(x.device):
+        _check(lib().rmsnorm_silu_gate_train_fwd(_ptr(x), _ptr(z), _ptr(w), wd, float(eps),
+                                                 C.byref(L), _ptr(y), _ptr(rstd), _stream(x)),
+               "rmsnorm_silu_gate_train_fwd")
     return y, rstd
 
 
@@ -258,8 +274,7 @@ def rmsnorm_silu_gate_train_bwd(dy: torch.Tensor, x: torch.Tensor, z: torch.Tens
                                 dw_dtype: torch.dtype = torch.float32):
     """dx, dz (BF16) and dw (FP32, or BF16 with dw_dtype=torch.bfloat16) of the
     SiLU-gated form."""
-    for t, n in ((dy, "dy"), (x, "x"), (z, "z"), (rstd, "rstd")):
-        _device(t, n)
+    _on_device(x, dy=dy, z=z, rstd=rstd, w=w, workspace=workspace)
     _inner_contiguous(x, "x")
     _inner_contiguous(dy, "dy")
     _same_geometry(x, z, "x", "z")
@@ -273,9 +288,11 @@ def rmsnorm_silu_gate_train_bwd(dy: torch.Tensor, x: torch.Tensor, z: torch.Tens
     dx = torch.empty(full, dtype=torch.bfloat16, device=x.device)
     dz = torch.empty(full, dtype=torch.bfloat16, device=x.device)
     dw, dwd = _dw(L.width, dw_dtype, x.device)
-    _check(lib().rmsnorm_silu_gate_train_bwd(_ptr(dy), _ptr(x), _ptr(z), _ptr(w), wd, _ptr(rstd),
-                                             int(bool(deterministic)), C.byref(L), _ptr(dx),
-                                             _ptr(dz), _ptr(dw), dwd, _ptr(ws), ws_bytes,
-                                             C.byref(launch) if launch else None, _stream(x)),
-           "rmsnorm_silu_gate_train_bwd")
+    with torch.cuda.device(x.device):
+        _check(lib().rmsnorm_silu_gate_train_bwd(_ptr(dy), _ptr(x), _ptr(z), _ptr(w), wd,
+                                                 _ptr(rstd), int(bool(deterministic)), C.byref(L),
+                                                 _ptr(dx), _ptr(dz), _ptr(dw), dwd, _ptr(ws),
+                                                 ws_bytes, C.byref(launch) if launch else None,
+                                                 _stream(x)),
+               "rmsnorm_silu_gate_train_bwd")
     return dx, dz, dw
