@@ -201,7 +201,7 @@ def sweep(out_path, reps=20):
     # Cold caches: read (not write) 512 MB between calls, evicting L2 and the
     # 256 MB Infinity Cache without leaving dirty lines whose write-back would
     # land inside the timed call.
-    flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)  # FP32 sum: one read pass, no cast
 
     def graph_time(fn):
         fn()  # allocations (outputs, workspace) happen outside capture
@@ -377,20 +377,26 @@ def sweep_spans(sweep_json, trace_dir):
         if c["case"] not in ranges or c["cfg"] == "-":
             continue
         t0, t1 = ranges[c["case"]]
-        spans, cur = [], None
+        spans, folds, cur = [], [], None
+
+        def close(cur):
+            spans.append(cur[1] - cur[0])
+            folds.append(cur[2])
+
         for s_, e_, name in kern:
             if s_ < t0 or s_ > t1:
                 continue
             if "rmsn::" not in name:  # the cache-flush read between replays
                 if cur:
-                    spans.append(cur[1] - cur[0])
+                    close(cur)
                 cur = None
             else:
-                cur = (s_, e_) if cur is None else (cur[0], max(cur[1], e_))
+                fold = e_ - s_ if "k_fold" in name else 0
+                cur = (s_, e_, fold) if cur is None else (cur[0], max(cur[1], e_), cur[2] + fold)
         if cur:
-            spans.append(cur[1] - cur[0])
+            close(cur)
         if spans:
-            out[(c["cfg"], c["workload"], c["op"])] = (spans, c["event_us"], c["bytes"])
+            out[(c["cfg"], c["workload"], c["op"])] = (spans, c["event_us"], c["bytes"], folds)
     return out
 
 
@@ -422,10 +428,11 @@ def sweep_kernels(args, out_md):
            "the HIP-event time around the replay (median of the processes), which carries a ~13 "
            "us floor on this system. GB/s uses the algorithmic bytes and the median: fwd 4TH, bwd "
            "6TH, residual 8TH each way, gate fwd 6TH and bwd 10TH (+ per-row and per-column "
-           "terms).", "",
+           "terms). The fold column is the median duration of the k_fold kernel inside the span "
+           "(large path only; the small path is one kernel).", "",
            "| cfg | workload | op | kernel-active us/call (median) | p10-p90 | per-process medians "
-           "| algorithmic GB/s | % of 8 TB/s | event us/call |",
-           "|---|---|---|---|---|---|---|---|---|"]
+           "| of which k_fold | algorithmic GB/s | % of 8 TB/s | event us/call |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
     for key in runs[0]:
         if not all(key in r for r in runs):
             continue
@@ -437,9 +444,12 @@ def sweep_kernels(args, out_md):
         ev = sorted(r[key][1] for r in runs)[n // 2]
         nbytes = runs[0][key][2]
         gbps = nbytes / (med * 1e3) if nbytes else None
+        folds = sorted(x for r in runs for x in r[key][3])
+        fold = folds[len(folds) // 2] / 1e3
         cfg, wl, op = key
         out.append(f"| {cfg} | {wl} | {op} | {med:.2f} | {p10:.2f}-{p90:.2f} | "
                    f"{' / '.join(f'{v:.2f}' for v in per)} | "
+                   f"{f'{fold:.2f}' if fold else '-'} | "
                    f"{f'{gbps:.0f}' if gbps else '-'} | "
                    f"{f'{100 * gbps / HBM_PEAK_GBPS:.1f}' if gbps else '-'} | {ev:.2f} |")
     with open(out_md, "w") as fh:
@@ -582,7 +592,7 @@ def main():
     if args.stats_report:
         stats_report(*args.stats_report,
                      "rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/prof_bench "
-                     "-o run -- python3 $REPO/bench.py --steps 20 --warmup 5 --no-cpu")
+                     "-o run -- python3 $REPO/bench.py")
         return
     if args.traffic_report:
         traffic_report(*args.traffic_report)
