@@ -410,14 +410,14 @@ def sweep_kernels(args, out_md):
     runs = [sweep_spans(args[i], args[i + 1]) for i in range(0, len(args), 2)]
     n = len(runs)
     names = "abcdefgh"[:n]
-    pairs = " ".join(f"$REPO/gpurun_out/sweep_{k}.md.json $REPO/gpurun_out/prof_sweep_{k}"
+    pairs = " ".join(f"$OUT/sweep_{k}.md.json $OUT/prof_sweep_{k}"
                      for k in names)
     out = ["# Every workload: kernel-active time per call, cold caches (rocprofv3)", "",
-           "Commands (repository root $REPO on the MI355X box; committed files only), "
+           "Commands (repository root $REPO, output directory $OUT, on an MI355X; committed files only), "
            f"{n} separate process{'es' if n > 1 else ''}, k = {', '.join(names)}:",
            "", "```", "cd /tmp && export TMPDIR=/tmp",
-           "rocprofv3 --kernel-trace --marker-trace --output-format csv -d $REPO/gpurun_out/prof_sweep_<k> "
-           "-o sweep -- python3 $REPO/bench.py --sweep $REPO/gpurun_out/sweep_<k>.md",
+           "rocprofv3 --kernel-trace --marker-trace --output-format csv -d $OUT/prof_sweep_<k> "
+           "-o sweep -- python3 $REPO/bench.py --sweep $OUT/sweep_<k>.md",
            f"python3 $REPO/bench.py --sweep-kernels {pairs} <this file>", "```", "",
            "Each call is one graph replay after a 512 MB read that evicts L2 and the Infinity Cache. "
            "Kernel-active span = first kernel start to last kernel end of the call (all of this "
@@ -463,7 +463,7 @@ def stats_report(stats_csv, out_md, command):
     import csv
 
     lines = ["# rocprofv3 kernel statistics: backward and forward at [131072, 4096] BF16 (w FP32)",
-             "", "Command (repository root $REPO on the MI355X box; committed files only):", "",
+             "", "Command (repository root $REPO, output directory $OUT, on an MI355X; committed files only):", "",
              "```", "cd /tmp && export TMPDIR=/tmp", command,
              f"python3 $REPO/bench.py --stats-report <run_kernel_stats.csv> <this file>", "```", "",
              f"Algorithmic bytes: backward call {bwd_bytes(T_HEAD, H_HEAD, 4):,} B; forward "
@@ -539,13 +539,13 @@ def traffic_report(fetch_dir, write_dir, out_json, out_md):
         json.dump(out, fh, indent=1)
     md = f"""# HBM traffic of the backward call at [131072, 4096] (rocprofv3 counters)
 
-Commands (repository root $REPO on the MI355X box; committed files only; one counter per run):
+Commands (repository root $REPO, output directory $OUT, on an MI355X; committed files only; one counter per run):
 
 ```
 cd /tmp && export TMPDIR=/tmp
-timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch -o run -- python3 $REPO/bench.py --traffic-probe
-timeout -s KILL 240 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write -o run -- python3 $REPO/bench.py --traffic-probe
-python3 $REPO/bench.py --traffic-report $REPO/gpurun_out/pmc_fetch $REPO/gpurun_out/pmc_write <json> <this file>
+timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_fetch -o run -- python3 $REPO/bench.py --traffic-probe
+timeout -s KILL 240 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/pmc_write -o run -- python3 $REPO/bench.py --traffic-probe
+python3 $REPO/bench.py --traffic-report $OUT/pmc_fetch $OUT/pmc_write <json> <this file>
 ```
 
 `bench.py --traffic-probe` runs one 1 GiB device-to-device copy (torch `copy_`, dispatched as
@@ -591,7 +591,7 @@ def main():
     args = ap.parse_args()
     if args.stats_report:
         stats_report(*args.stats_report,
-                     "rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/prof_bench "
+                     "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof_bench "
                      "-o run -- python3 $REPO/bench.py")
         return
     if args.traffic_report:
@@ -601,7 +601,7 @@ def main():
         sweep_kernels(args.sweep_kernels[:-1], args.sweep_kernels[-1])
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: this benchmark runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by rows with one dw all-reduce; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
