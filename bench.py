@@ -162,9 +162,13 @@ def host_cpu():
     return {"model": model, "cpus_available": avail}
 
 
+GATE_T = 16384  # gated form measured by the counter runs: [16384, 4096]
+
+
 def traffic_probe():
     """For rocprofv3 --pmc runs: one plain copy of known size (calibration),
-    then three backward calls at the headline shape."""
+    then three forward and three backward calls at the headline shape, and
+    three gated forward and backward calls at [16384, 4096]."""
     import torch
 
     import rmsnorm_train_fwd_amd as R
@@ -181,9 +185,19 @@ def traffic_probe():
     x = p.x.to(dev).view(T_HEAD, H_HEAD)
     dy = p.dy.to(dev).view(T_HEAD, H_HEAD)
     w = p.w.to(dev)
-    _, rstd = R.rmsnorm_train_fwd(x, w, p.eps)
+    for _ in range(3):
+        _, rstd = R.rmsnorm_train_fwd(x, w, p.eps)
     for _ in range(3):
         R.rmsnorm_train_bwd(dy, x, rstd, w, False)
+    torch.cuda.synchronize()
+    del x, dy, rstd
+    g = synth.make(GATE_T, H_HEAD, seed=0, w_dtype="f32", form="gate")
+    x, z = g.x.to(dev).view(GATE_T, H_HEAD), g.extra.to(dev).view(GATE_T, H_HEAD)
+    dy, w = g.dy.to(dev).view(GATE_T, H_HEAD), g.w.to(dev)
+    for _ in range(3):
+        _, rstd = R.rmsnorm_silu_gate_train_fwd(x, z, w, g.eps)
+    for _ in range(3):
+        R.rmsnorm_silu_gate_train_bwd(dy, x, z, rstd, w, False)
     torch.cuda.synchronize()
     print("[bench] traffic probe done", file=sys.stderr, flush=True)
 
@@ -522,7 +536,16 @@ def traffic_report(fetch_dir, write_dir, out_json, out_md):
         v = [float(r["Counter_Value"]) * 1024 * factor for r in rows if key in r["Kernel_Name"]]
         return sum(v) / len(v)
 
-    kr, kw = per(F, "k_bwd_large", ff), per(W, "k_bwd_large", wf)
+    plain_bwd = f"k_bwd_large<{H_HEAD}, true, 0, false"
+    kr, kw = per(F, plain_bwd, ff), per(W, plain_bwd, wf)
+    plain_fwd, gate_fwd = f"k_fwd<{H_HEAD}, true, 0,", f"k_fwd<{H_HEAD}, true, 2,"
+    gate_bwd = f"k_bwd_large<{H_HEAD}, true, 2, false"
+    fwr, fww = per(F, plain_fwd, ff), per(W, plain_fwd, wf)
+    gfr, gfw = per(F, gate_fwd, ff), per(W, gate_fwd, wf)
+    gbr, gbw = per(F, gate_bwd, ff), per(W, gate_bwd, wf)
+    TH, GH = T_HEAD * H_HEAD, GATE_T * H_HEAD
+    alg_fwd = fwd_bytes(T_HEAD, H_HEAD, 4)
+    alg_gf, alg_gb = 6 * GH + 4 * GATE_T + 4 * H_HEAD, 10 * GH + 4 * GATE_T + 8 * H_HEAD
     import torch
     import rmsnorm_train_fwd_amd as R
     chunks = R.rmsnorm_train_bwd_query(torch.empty((T_HEAD, H_HEAD), dtype=torch.bfloat16), False).chunks
@@ -534,6 +557,16 @@ def traffic_report(fetch_dir, write_dir, out_json, out_md):
            "ratio_to_algorithmic": round(total / alg, 5), "fetch_scale": round(ff, 6),
            "write_scale": round(wf, 6), "k_bwd_large": {"read": round(kr), "write": round(kw)},
            "k_fold": {"read": round(fr), "write": round(fw)},
+           "forward": {"workload": "rmsnorm_train_fwd [131072,4096] BF16, w FP32",
+                       "read": round(fwr), "write": round(fww), "algorithmic": alg_fwd,
+                       "ratio_to_algorithmic": round((fwr + fww) / alg_fwd, 5)},
+           "gate_forward": {"workload": "rmsnorm_silu_gate_train_fwd [16384,4096] BF16, w FP32",
+                            "read": round(gfr), "write": round(gfw), "algorithmic": alg_gf,
+                            "ratio_to_algorithmic": round((gfr + gfw) / alg_gf, 5)},
+           "gate_backward_main": {"workload": "rmsnorm_silu_gate_train_bwd non-deterministic "
+                                  "[16384,4096] BF16, w FP32 (main kernel; k_fold as above)",
+                                  "read": round(gbr), "write": round(gbw), "algorithmic": alg_gb,
+                                  "ratio_to_algorithmic": round((gbr + gbw) / alg_gb, 5)},
            "calibration_kib": {"fetch": copy_kib(F), "write": copy_kib(W)}}
     with open(out_json, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -549,7 +582,8 @@ python3 $REPO/bench.py --traffic-report $OUT/pmc_fetch $OUT/pmc_write <json> <th
 ```
 
 `bench.py --traffic-probe` runs one 1 GiB device-to-device copy (torch `copy_`, dispatched as
-`__amd_rocclr_copyBuffer`), the forward once and the non-deterministic backward three times.
+`__amd_rocclr_copyBuffer`), the forward and the non-deterministic backward three times each at
+[131072, 4096], then the gated forward and backward three times each at [16384, 4096].
 Calibration with that copy of known size (1 GiB read, 1 GiB written): FETCH_SIZE read
 {copy_kib(F):.1f} KiB and WRITE_SIZE {copy_kib(W):.1f} KiB, so read bytes = FETCH_SIZE x 1024 x
 {ff:.5f} and written bytes = WRITE_SIZE x 1024 x {wf:.5f}.
@@ -559,11 +593,20 @@ Calibration with that copy of known size (1 GiB read, 1 GiB written): FETCH_SIZE
 | k_bwd_large<4096, w FP32, plain, non-det> | {kr / 1e9:.4f} GB | {kw / 1e9:.4f} GB |
 | k_fold | {fr / 1e9:.4f} GB | {fw / 1e6:.3f} MB |
 | **backward call** | **{(kr + fr) / 1e9:.4f} GB** | **{(kw + fw) / 1e9:.4f} GB** |
+| k_fwd<4096, w FP32, plain> [131072, 4096] | {fwr / 1e9:.4f} GB | {fww / 1e9:.4f} GB |
+| k_fwd<4096, w FP32, gate> [16384, 4096] | {gfr / 1e9:.4f} GB | {gfw / 1e9:.4f} GB |
+| k_bwd_large<4096, w FP32, gate, non-det> [16384, 4096] | {gbr / 1e9:.4f} GB | {gbw / 1e9:.4f} GB |
 
 Algorithmic: reads x, dy, rstd, w = {(4 * T_HEAD * H_HEAD + 4 * T_HEAD + 4 * H_HEAD) / 1e9:.4f} GB;
 writes dx, dw = {(2 * T_HEAD * H_HEAD + 4 * H_HEAD) / 1e9:.4f} GB; total {alg / 1e9:.4f} GB.
 Measured {total / 1e9:.4f} GB per call, {100 * (total / alg - 1):.2f}% above it: the FP64 chunk
 partials ({chunks} x {H_HEAD} x 8 B = {chunks * H_HEAD * 8 / 2**20:.0f} MiB) written by the main kernel and read back by the fold.
+Forward at [131072, 4096]: algorithmic x read, y and rstd written, w read =
+{alg_fwd / 1e9:.4f} GB; measured {(fwr + fww) / 1e9:.4f} GB ({100 * ((fwr + fww) / alg_fwd - 1):+.2f}%).
+Gated form at [16384, 4096]: forward algorithmic (x, z read; y, rstd written; w) {alg_gf / 1e9:.4f} GB,
+measured {(gfr + gfw) / 1e9:.4f} GB ({100 * ((gfr + gfw) / alg_gf - 1):+.2f}%); backward main kernel
+algorithmic (x, dy, z, rstd, w read; dx, dz written; dw) {alg_gb / 1e9:.4f} GB, measured
+{(gbr + gbw) / 1e9:.4f} GB ({100 * ((gbr + gbw) / alg_gb - 1):+.2f}%, its chunk partials included).
 x, dy and dx are each moved once. Kernel sources hash: {out['kernel_hash']} (bench.py reports
 `traffic` only while the current sources hash to this value).
 """
