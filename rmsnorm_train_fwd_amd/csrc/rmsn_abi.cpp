@@ -23,17 +23,17 @@ constexpr int32_t kMaxGrid = 1 << 24;
 // Small row counts, per width: at or below these, the dw tree gives each
 // chunk at most kSmallTreeTiles tiles, and the backward runs as one launch
 // (row tasks + column tasks) unless a launch override says otherwise. The
-// values are where the single launch stopped beating main kernel + fold on
-// MI355X (back-to-back calls, launch cost included); the column tasks re-read
-// x and dy over width / columns-per-task workgroups, so the crossover falls as
-// rows get wider. Both paths give the same bits.
+// values are where the single launch stopped beating main kernel + fold
+// (above them, on its tree of up to 256 chunks) on MI355X, kernel-active time
+// with cold caches; the column tasks re-read x and dy, so the crossover falls
+// as rows get wider. Both paths give the same bits for a given tree.
 int64_t small_rows(int64_t width) {
   switch (width) {
     case 256: return 2048;
-    case 512: return 2048;
-    case 1536: return 1024;
-    case 2048: return 1024;
-    case 4096: return 768;
+    case 512: return 1024;
+    case 1536: return 768;
+    case 2048: return 768;
+    case 4096: return 640;
     case 5120: return 512;
     default: return 384;  // 6144
   }

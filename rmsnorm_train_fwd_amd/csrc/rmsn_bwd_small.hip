@@ -24,13 +24,13 @@ hipError_t small_width(bool w_f32, int form, const BwdArgs& a, int rg, int cg, h
 
 int small_col_tile(int H) {
   switch (H) {
-    case 256: return SmallGeo<256>::BLOCK / (kFoldGroup * Geo<256>::R) * 8;
-    case 512: return SmallGeo<512>::BLOCK / (kFoldGroup * Geo<512>::R) * 8;
-    case 1536: return SmallGeo<1536>::BLOCK / (kFoldGroup * Geo<1536>::R) * 8;
-    case 2048: return SmallGeo<2048>::BLOCK / (kFoldGroup * Geo<2048>::R) * 8;
-    case 4096: return SmallGeo<4096>::BLOCK / (kFoldGroup * Geo<4096>::R) * 8;
-    case 5120: return SmallGeo<5120>::BLOCK / (kFoldGroup * Geo<5120>::R) * 8;
-    case 6144: return SmallGeo<6144>::BLOCK / (kFoldGroup * Geo<6144>::R) * 8;
+    case 256: return SmallGeo<256>::BLOCK / (kFoldGroup * Geo<256>::R) * SmallGeo<256>::CPT;
+    case 512: return SmallGeo<512>::BLOCK / (kFoldGroup * Geo<512>::R) * SmallGeo<512>::CPT;
+    case 1536: return SmallGeo<1536>::BLOCK / (kFoldGroup * Geo<1536>::R) * SmallGeo<1536>::CPT;
+    case 2048: return SmallGeo<2048>::BLOCK / (kFoldGroup * Geo<2048>::R) * SmallGeo<2048>::CPT;
+    case 4096: return SmallGeo<4096>::BLOCK / (kFoldGroup * Geo<4096>::R) * SmallGeo<4096>::CPT;
+    case 5120: return SmallGeo<5120>::BLOCK / (kFoldGroup * Geo<5120>::R) * SmallGeo<5120>::CPT;
+    case 6144: return SmallGeo<6144>::BLOCK / (kFoldGroup * Geo<6144>::R) * SmallGeo<6144>::CPT;
     default: return 0;
   }
 }

@@ -419,21 +419,39 @@ __global__ __launch_bounds__(kFoldThreads) void k_fold(const double* __restrict_
                                                        void* __restrict__ dw, int dw_bf16, int H,
                                                        int64_t chunks);
 
-// Small-row backward in one launch. Workgroups [0, row_grid) are row tasks
-// (dx, strided over row tiles of RS rows); the rest are column tasks (dw),
-// strided over column tiles. A column-task thread (cv, q, kl) owns 8 columns,
-// sub-chain q of chunk kl of the current fold group: it loads row q of the
-// chunk's tiles 8 tiles at a time (one memory round trip; the tree gives a
-// chunk at most 8 tiles when the row count is small) and runs Dot2 over them
-// in ascending order, exactly as k_bwd_large does. Through LDS, the chunk
+// Small-row backward in one launch. The first col_grid workgroups are column
+// tasks (dw), strided over column tiles, and are dispatched first because
+// they are the longer tasks; the last row_grid workgroups are row tasks (dx,
+// strided over row tiles of RS rows). A column-task thread (cv, q, kl) owns
+// CPT columns, sub-chain q of chunk kl of the current fold group: it loads
+// row q of the chunk's tiles 8 tiles at a time (one memory round trip; the
+// tree gives a chunk at most 8 tiles when the row count is small) and runs
+// Dot2 over them in ascending order, exactly as k_bwd_large does. Through LDS, the chunk
 // partial is then 0.0 + d_0 + ... + d_{R-1} in sub-chain order, and the fold
 // follows k_fold's order. rstd is an input, so dw needs nothing from the row
 // tasks and no workgroup ever waits for another.
-// Workgroup size of the small path: the main kernel's, capped at 512 threads
+// 2 or 4 BF16 values loaded as one 4- or 8-byte word.
+template <int N> struct VecOf;
+template <> struct VecOf<2> {
+  typedef uint32_t T;
+  __device__ static void unpack(T u, float (&f)[2]) { f[0] = bf_lo(u); f[1] = bf_hi(u); }
+};
+template <> struct VecOf<4> {
+  typedef uint2 T;
+  __device__ static void unpack(T u, float (&f)[4]) {
+    f[0] = bf_lo(u.x); f[1] = bf_hi(u.x); f[2] = bf_lo(u.y); f[3] = bf_hi(u.y);
+  }
+};
+
+// Small-path shape. Workgroup size: the main kernel's, capped at 512 threads
 // (a row task needs whole row groups; the dw tree only needs the sub-chain
-// count R, which stays that of the main kernel).
+// count R, which stays that of the main kernel). CPT: columns per column-task
+// thread; the dw work of a call is (chunks x R x width / CPT) threads, so a
+// narrower slice per thread spreads it over more workgroups (2 at widths up
+// to 512, 4 above; 8 measured slower everywhere).
 template <int H>
 struct SmallGeo {
+  static constexpr int CPT = H <= 512 ? 2 : 4;
   static constexpr int BLOCK = Geo<H>::BLOCK > 768 ? 512 : Geo<H>::BLOCK;
   static constexpr int RS = BLOCK / Geo<H>::TPR;  // rows per row-task tile
   static_assert(RS >= 1 && RS * Geo<H>::TPR == BLOCK, "row tasks hold whole row groups");
@@ -445,18 +463,20 @@ __global__ __launch_bounds__(SmallGeo<H>::BLOCK) void k_bwd_small(BwdArgs a, int
   constexpr int R = G::R, TPR = G::TPR, BLOCK = SmallGeo<H>::BLOCK, RS = SmallGeo<H>::RS;
   constexpr int KL = kFoldGroup;               // chunk lanes: one pass = one fold group
   constexpr int CV = BLOCK / (KL * R);         // column vectors per tile
-  constexpr int kTile = CV * 8;                // columns per tile
+  constexpr int CPT = SmallGeo<H>::CPT;        // columns per thread
+  constexpr int kTile = CV * CPT;              // columns per tile
   static_assert(CV >= 1 && CV * KL * R == BLOCK, "column-task layout");
   static_assert(H % kTile == 0, "column tiles must cover the row exactly");
   __shared__ float slots[RowSum<G, 1>::kSlots];
   __shared__ double part[KL][R][kTile];
-  if ((int)blockIdx.x < row_grid) {
+  const int col_grid = gridDim.x - row_grid;
+  if ((int)blockIdx.x >= col_grid) {
     const int q = row_group<G>(), lane = threadIdx.x % TPR;
     int parity = 0;
     float wr[G::E];
     load_w<G, WF32>(a.w, lane, wr);
     const int64_t tiles = (a.rows + RS - 1) / RS;
-    for (int64_t t = blockIdx.x; t < tiles; t += row_grid) {
+    for (int64_t t = blockIdx.x - col_grid; t < tiles; t += row_grid) {
       bool ok[1] = {t * RS + q < a.rows};
       int64_t row[1] = {ok[0] ? t * RS + q : t * RS};
       RowBatch<H, FORM, 1> rb;
@@ -468,12 +488,11 @@ __global__ __launch_bounds__(SmallGeo<H>::BLOCK) void k_bwd_small(BwdArgs a, int
   const int cv = threadIdx.x % CV;
   const int q = (threadIdx.x / CV) % R;
   const int kl = threadIdx.x / (CV * R);
-  const int col_grid = gridDim.x - row_grid;
   const int64_t K = a.chunks;
   const int64_t groups = (K + KL - 1) / KL;
-  for (int tile = blockIdx.x - row_grid; tile < H / kTile; tile += col_grid) {
-    const int c0 = tile * kTile + cv * 8;
-    double total = 0.0;  // column c0 + kl, on threads (cv, q = 0, kl < 8)
+  for (int tile = blockIdx.x; tile < H / kTile; tile += col_grid) {
+    const int c0 = tile * kTile + cv * CPT;
+    double total = 0.0;  // column c0 + kl, on threads (cv, q = 0, kl < CPT)
     for (int64_t g = 0; g < groups; ++g) {
       const int64_t k = g * KL + kl;
       if (k < K) {
@@ -483,10 +502,11 @@ __global__ __launch_bounds__(SmallGeo<H>::BLOCK) void k_bwd_small(BwdArgs a, int
         // the loop runs) and are skipped.
         const int64_t r0 = k * R;
         const int64_t step = K * R;
-        Dot2 acc[8];
+        Dot2 acc[CPT];
         constexpr int NB = 8;  // tiles per round trip
         for (int64_t rb = r0 + q; rb - q < a.rows; rb += NB * step) {
-          uint4 xv[NB], gv[NB], zv[NB];
+          using VT = typename VecOf<CPT>::T;
+          VT xv[NB], gv[NB], zv[NB];
           float rr[NB];
           bool ok[NB];
 #pragma unroll
@@ -495,19 +515,20 @@ __global__ __launch_bounds__(SmallGeo<H>::BLOCK) void k_bwd_small(BwdArgs a, int
             ok[i] = row < a.rows;
             const int64_t rc = ok[i] ? row : r0;
             rr[i] = a.rstd[rc];
-            xv[i] = ld16(a.x.p + row_off(a.x, rc, a.heads) + c0);
-            gv[i] = ld16(a.dy.p + row_off(a.dy, rc, a.heads) + c0);
-            if constexpr (FORM == kGate) zv[i] = ld16(a.e.p + row_off(a.e, rc, a.heads) + c0);
+            xv[i] = *reinterpret_cast<const VT*>(a.x.p + row_off(a.x, rc, a.heads) + c0);
+            gv[i] = *reinterpret_cast<const VT*>(a.dy.p + row_off(a.dy, rc, a.heads) + c0);
+            if constexpr (FORM == kGate)
+              zv[i] = *reinterpret_cast<const VT*>(a.e.p + row_off(a.e, rc, a.heads) + c0);
           }
 #pragma unroll
           for (int i = 0; i < NB; ++i) {
             if (!ok[i]) continue;
-            float xf[8], gf[8], zf[8];
-            unpack8(xv[i], xf);
-            unpack8(gv[i], gf);
-            if constexpr (FORM == kGate) unpack8(zv[i], zf);
+            float xf[CPT], gf[CPT], zf[CPT];
+            VecOf<CPT>::unpack(xv[i], xf);
+            VecOf<CPT>::unpack(gv[i], gf);
+            if constexpr (FORM == kGate) VecOf<CPT>::unpack(zv[i], zf);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < CPT; ++e) {
               float b = rr[i];
               if constexpr (FORM == kGate) b = rr[i] * (zf[e] * sigmoid_f(zf[e]));
               acc[e].add(gf[e] * xf[e], b);
@@ -515,29 +536,29 @@ __global__ __launch_bounds__(SmallGeo<H>::BLOCK) void k_bwd_small(BwdArgs a, int
           }
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) part[kl][q][cv * 8 + e] = acc[e].value();
+        for (int e = 0; e < CPT; ++e) part[kl][q][cv * CPT + e] = acc[e].value();
       }
       __syncthreads();
       if (q == 0 && k < K) {
         // chunk partial: 0.0 + d_0 + d_1 + ... in sub-chain order
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < CPT; ++e) {
           double p = 0.0;
-          for (int qq = 0; qq < R; ++qq) p = p + part[kl][qq][cv * 8 + e];
-          part[kl][0][cv * 8 + e] = p;
+          for (int qq = 0; qq < R; ++qq) p = p + part[kl][qq][cv * CPT + e];
+          part[kl][0][cv * CPT + e] = p;
         }
       }
       __syncthreads();
       // Group fold, one thread per column (thread (cv, 0, kl) takes column
       // c0 + kl): the group's chunk partials in ascending order from 0.0,
       // read from LDS 8 at a time ahead of the adds.
-      if (q == 0 && kl < 8) {
+      if (q == 0 && kl < CPT) {
         const int n = (int)(K - g * KL < KL ? K - g * KL : KL);
         double s = 0.0;
         for (int k0 = 0; k0 < n; k0 += 8) {
           double v[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = k0 + i < n ? part[k0 + i][0][cv * 8 + kl] : 0.0;
+          for (int i = 0; i < 8; ++i) v[i] = k0 + i < n ? part[k0 + i][0][cv * CPT + kl] : 0.0;
 #pragma unroll
           for (int i = 0; i < 8; ++i)
             if (k0 + i < n) s = s + v[i];
@@ -546,7 +567,7 @@ __global__ __launch_bounds__(SmallGeo<H>::BLOCK) void k_bwd_small(BwdArgs a, int
       }
       __syncthreads();
     }
-    if (q == 0 && kl < 8) store_dw(a.dw, a.dw_bf16, c0 + kl, total);
+    if (q == 0 && kl < CPT) store_dw(a.dw, a.dw_bf16, c0 + kl, total);
   }
 }
 
