@@ -149,3 +149,28 @@ def test_det_dw_bits_follow_the_documented_tree_under_cancellation(H, rows, path
     got = dw.cpu().numpy()
     diff = np.flatnonzero(got.view(np.uint32) != want.view(np.uint32))
     assert diff.size == 0, f"{diff.size} of {H} columns differ from the documented tree"
+
+
+# Row counts where the tree switches from at most 8 tiles per chunk (and the
+# single-launch path) to up to 256 chunks (main kernel + fold): S(width).
+SMALL_ROWS = {256: 2048, 512: 1024, 1536: 768, 2048: 768, 4096: 640, 5120: 512, 6144: 384}
+
+
+@pytest.mark.parametrize("path", [R.PATH_LARGE, R.PATH_SMALL], ids=["large", "small"])
+@pytest.mark.parametrize("above", [0, 1], ids=["S", "S+1"])
+@pytest.mark.parametrize("H", [256, 512, 1536, 2048, 4096, 5120, 6144])
+def test_det_dw_bits_at_the_small_row_limit(H, above, path):
+    rows = SMALL_ROWS[H] + above
+    X, DY, rs = cancellation_rows(rows, H, seed=7 * H + rows)
+    x, dy, r32 = X.float().numpy(), DY.float().numpy(), rs.numpy()
+    xg, dyg = X.cuda(), DY.cuda()
+    plan = R.rmsnorm_train_bwd_query(xg, True)
+    tiles = -(-rows // plan.subchains)
+    assert plan.chunks == (min(tiles, 256) if above else -(-tiles // 8))
+    assert plan.path == (R.PATH_LARGE if above else R.PATH_SMALL)
+    want = emulate_det_dw(x, dy, r32, plan.subchains, plan.chunks)
+    _, dw = R.rmsnorm_train_bwd(dyg, xg, rs.cuda(), torch.ones(H, device="cuda"), True,
+                                launch=R.Launch(0, 0, path))
+    got = dw.cpu().numpy()
+    diff = np.flatnonzero(got.view(np.uint32) != want.view(np.uint32))
+    assert diff.size == 0, f"{diff.size} of {H} columns differ from the documented tree"
