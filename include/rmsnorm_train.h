@@ -103,7 +103,9 @@ enum {
 };
 
 /* Launch override, for tests of grid independence. NULL = automatic.
- * grid / fold_grid: 1-D workgroup counts (0 = automatic; >= 1 otherwise). */
+ * grid / fold_grid: 1-D workgroup counts (0 = automatic; >= 1 otherwise) of
+ * the main kernel and the fold on the large path, and of the row tasks (dx)
+ * and the column tasks (dw) of the single launch on the small path. */
 typedef struct {
   int32_t grid;
   int32_t fold_grid;
@@ -117,8 +119,8 @@ typedef struct {
   int64_t chunks;        /* K: chunks of the dw tree (see rmsnorm_train_bwd) */
   int32_t subchains;     /* R: rows per tile = sub-chains per chunk (fixed per width) */
   int32_t fold_group;    /* chunks per first-level fold group */
-  int32_t grid;          /* workgroups of the main (or single) launch */
-  int32_t fold_grid;     /* workgroups of the fold launch (0 on the small path) */
+  int32_t grid;          /* large path: main-kernel workgroups; small path: row tasks */
+  int32_t fold_grid;     /* large path: fold workgroups; small path: column tasks */
   size_t workspace_bytes;
 } rmsn_bwd_plan;
 
