@@ -291,7 +291,8 @@ __global__ __launch_bounds__(Geo<H>::BLOCK) void k_bwd_large(BwdArgs a) {
   static_assert(8 % D == 0, "a batch must not straddle a flush of the 8-row blocks");
   const int q = row_group<G>(), lane = threadIdx.x % TPR;
   __shared__ float slots[RowSum<G, D>::kSlots];
-  __shared__ double merge[R > 1 ? H : 1];
+  // R >= 4: every sub-chain's values at once, [R][H]; R == 2: a running sum, [H].
+  __shared__ double merge[R >= 4 ? R * H : (R > 1 ? H : 1)];
   int parity = 0;
   float wr[E];
   load_w<G, WF32>(a.w, lane, wr);
@@ -386,6 +387,20 @@ __global__ __launch_bounds__(Geo<H>::BLOCK) void k_bwd_large(BwdArgs a) {
         for (int i = 0; i < 4; ++i)
           o[i] = make_double2(0.0 + dv[v * 8 + 2 * i], 0.0 + dv[v * 8 + 2 * i + 1]);
       }
+    } else if constexpr (R >= 4) {
+      // p = 0.0 + d_0 + d_1 + ... + d_{R-1}, in row-group order, one thread
+      // per column after a single barrier.
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) merge[q * H + elem0<G>(v, lane) + i] = dv[v * 8 + i];
+      __syncthreads();
+      for (int i = threadIdx.x; i < H; i += G::BLOCK) {
+        double p = 0.0;
+        for (int qq = 0; qq < R; ++qq) p = p + merge[qq * H + i];
+        out[i] = p;
+      }
+      __syncthreads();
     } else {
       // p = 0.0 + d_0 + d_1 + ... + d_{R-1}, in row-group order.
       for (int qq = 0; qq < R; ++qq) {
