@@ -162,6 +162,103 @@ def host_cpu():
     return {"model": model, "cpus_available": avail}
 
 
+def cpu_sweep(out_md, reps=3):
+    """The FP64 oracle (single-threaded C) timed on every workload of the
+    configurations: each call runs on a sample of at most 2^24 elements of the
+    workload's rows (the oracle's cost is linear in the row count), median of
+    reps, scaled to the full row count. Writes a markdown table."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from rmsnorm_train_fwd_amd import synth
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    def med_time(fn):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[len(ts) // 2]
+
+    rows_out = []
+
+    def add(cfg, workload, op, rows, sample_rows, dt, nbytes):
+        us = dt * 1e6 * rows / sample_rows
+        rows_out.append((cfg, workload, op, sample_rows, dt, us, nbytes / (us * 1e-6) / 1e9))
+        print(f"[cpu] {cfg:3s} {workload:32s} {op:4s} {us:14.1f} us", file=sys.stderr, flush=True)
+
+    def views(p, form):
+        def v(buf):
+            return oracle.View(bits(buf), p.T, p.heads, p.width, p.row_stride, p.head_stride)
+        return v(p.x), v(p.dy), (v(p.extra) if form != "plain" else None), \
+            (v(p.dh) if form == "residual" else None)
+
+    def run(cfg, T, W, heads=1, rs=None, hs=None, form="plain", w_dtype="f32", ops=("fwd", "bwd"),
+            label=None):
+        rows = T * heads
+        ts = max(1, min(T, (1 << 24) // (W * heads)))
+        p = synth.make(ts, W, seed=0, heads=heads, w_dtype=w_dtype, form=form, row_stride=rs,
+                       head_stride=hs)
+        x, dy, e, dh = views(p, form)
+        w = p.w.double().numpy()
+        wb = 4 if w_dtype == "f32" else 2
+        n, sr = rows * W, ts * heads
+        name = label or f"[{T},{W}]"
+        if "fwd" in ops:
+            if form == "plain":
+                dt = med_time(lambda: oracle.fwd(x, w, p.eps))
+                add(cfg, name, "fwd", rows, sr, dt, 4 * n + 4 * rows + wb * W)
+            elif form == "residual":
+                dt = med_time(lambda: oracle.res_fwd(x, e, w, p.eps))
+                add(cfg, name, "fwd", rows, sr, dt, 8 * n + 4 * rows + wb * W)
+            else:
+                dt = med_time(lambda: oracle.gate_fwd(x, e, w, p.eps))
+                add(cfg, name, "fwd", rows, sr, dt, 6 * n + 4 * rows + wb * W)
+        if "bwd" in ops:
+            if form == "plain":
+                dt = med_time(lambda: oracle.bwd(dy, x, w, p.eps))
+                add(cfg, name, "bwd", rows, sr, dt, 6 * n + 4 * rows + wb * W + 4 * W)
+            elif form == "residual":
+                dt = med_time(lambda: oracle.bwd(dy, x, w, p.eps, dh=dh))
+                add(cfg, name, "bwd", rows, sr, dt, 8 * n + 4 * rows + wb * W + 4 * W)
+            else:
+                dt = med_time(lambda: oracle.gate_bwd(dy, x, e, w, p.eps))
+                add(cfg, name, "bwd", rows, sr, dt, 10 * n + 4 * rows + wb * W + 4 * W)
+
+    run("1", 8, 512, w_dtype="bf16")
+    for W in (512, 1536, 2048, 4096, 5120, 6144):
+        run("2", 203, W, ops=("bwd",))
+    for rs_, hs_ in ((12288, 512), (6144, 256)):
+        run("2", 203, 256, heads=24, rs=rs_, hs=hs_, ops=("bwd",),
+            label=f"[203,24,256] strides ({rs_},{hs_},1)")
+    for W in (1536, 2048, 4096, 5120, 6144):
+        run("3", 131072, W)
+    run("4", 131072, 6144, form="residual", label="[131072,6144] residual")
+    for T in (3534, 8192, 16384):
+        run("5", T, 4096, form="gate", label=f"[{T},4096] gate")
+    host = host_cpu()
+    lines = ["# FP64 CPU oracle on every workload (single-threaded C)", "",
+             "Command (repository root $REPO, on the MI355X host; committed files only):", "",
+             "```", "python3 $REPO/bench.py --cpu-sweep <this file>", "```", "",
+             f"Host: {host['model']}, {host['cpus_available']} logical CPUs available; the oracle "
+             "uses one thread (cores = 1). Each call runs on a sample of at most 2^24 elements "
+             f"of the workload's rows, median of {reps} runs, and is scaled to the full row count "
+             "(the oracle's cost is linear in the rows). GB/s uses the same algorithmic bytes as "
+             "the GPU tables: fwd 4TH, bwd 6TH, residual 8TH each way, gate fwd 6TH and bwd 10TH "
+             "(+ per-row and per-column terms).", "",
+             "| cfg | workload | op | rows timed | s per sample | us per full call | GB/s |",
+             "|---|---|---|---|---|---|---|"]
+    for cfg, wl, op, sr, dt, us, gbps in rows_out:
+        lines.append(f"| {cfg} | {wl} | {op} | {sr} | {dt:.4f} | {us:.1f} | {gbps:.3f} |")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 GATE_T = 16384  # gated form measured by the counter runs: [16384, 4096]
 
 
@@ -629,6 +726,8 @@ def main():
     ap.add_argument("--sweep-kernels", nargs="+", metavar="ARG",
                     help="kernel-active times of a --sweep run traced by rocprofv3")
     ap.add_argument("--stats-report", nargs=2, metavar=("KERNEL_STATS.csv", "OUT.md"))
+    ap.add_argument("--cpu-sweep", metavar="OUT.md",
+                    help="time the FP64 CPU oracle on every workload (no GPU)")
     ap.add_argument("--traffic-report", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "OUT.json", "OUT.md"))
     args = ap.parse_args()
@@ -639,6 +738,9 @@ def main():
         return
     if args.traffic_report:
         traffic_report(*args.traffic_report)
+        return
+    if args.cpu_sweep:
+        cpu_sweep(args.cpu_sweep)
         return
     if args.sweep_kernels:
         sweep_kernels(args.sweep_kernels[:-1], args.sweep_kernels[-1])
