@@ -434,17 +434,6 @@ __global__ __launch_bounds__(kFoldThreads) void k_fold(const double* __restrict_
                                                        void* __restrict__ dw, int dw_bf16, int H,
                                                        int64_t chunks);
 
-// Small-row backward in one launch. The first col_grid workgroups are column
-// tasks (dw), strided over column tiles, and are dispatched first because
-// they are the longer tasks; the last row_grid workgroups are row tasks (dx,
-// strided over row tiles of RS rows). A column-task thread (cv, q, kl) owns
-// CPT columns, sub-chain q of chunk kl of the current fold group: it loads
-// row q of the chunk's tiles 8 tiles at a time (one memory round trip; the
-// tree gives a chunk at most 8 tiles when the row count is small) and runs
-// Dot2 over them in ascending order, exactly as k_bwd_large does. Through LDS, the chunk
-// partial is then 0.0 + d_0 + ... + d_{R-1} in sub-chain order, and the fold
-// follows k_fold's order. rstd is an input, so dw needs nothing from the row
-// tasks and no workgroup ever waits for another.
 // 2 or 4 BF16 values loaded as one 4- or 8-byte word.
 template <int N> struct VecOf;
 template <> struct VecOf<2> {
@@ -472,6 +461,17 @@ struct SmallGeo {
   static_assert(RS >= 1 && RS * Geo<H>::TPR == BLOCK, "row tasks hold whole row groups");
 };
 
+// Small-row backward in one launch. The first col_grid workgroups are column
+// tasks (dw), strided over column tiles, and are dispatched first because
+// they are the longer tasks; the last row_grid workgroups are row tasks (dx,
+// strided over row tiles of RS rows). A column-task thread (cv, q, kl) owns
+// CPT columns, sub-chain q of chunk kl of the current fold group: it loads
+// row q of the chunk's tiles 8 tiles at a time (one memory round trip; the
+// tree gives a chunk at most 8 tiles when the row count is small) and runs
+// Dot2 over them in ascending order, exactly as k_bwd_large does. Through
+// LDS, the chunk partial is then 0.0 + d_0 + ... + d_{R-1} in sub-chain
+// order, and the fold follows k_fold's order. rstd is an input, so dw needs
+// nothing from the row tasks and no workgroup ever waits for another.
 template <int H, bool WF32, int FORM>
 __global__ __launch_bounds__(SmallGeo<H>::BLOCK) void k_bwd_small(BwdArgs a, int row_grid) {
   using G = Geo<H>;
