@@ -9,6 +9,8 @@
 - Calls honour the caller's stream.
 - Another stream keeping the GPU busy does not change any bit of the result
   (no workgroup ever waits for another: the pages' "stall" concern).
+- The backward workspace needs no initialisation: whatever it holds on entry
+  (NaN bytes, another call's partials) the results are the same bits.
 """
 import numpy as np
 import pytest
@@ -120,3 +122,27 @@ def test_busy_gpu_does_not_change_results():
     assert torch.equal(dx.view(torch.int16), dx0.view(torch.int16))
     assert torch.equal(dw.view(torch.int32), dw0.view(torch.int32))
     assert torch.isfinite(a).all()
+
+
+@pytest.mark.parametrize("det", [True, False])
+@pytest.mark.parametrize("T,H", [(4099, 4096), (65537, 1536), (3000, 256)])
+def test_workspace_contents_on_entry_do_not_matter(T, H, det):
+    p = synth.make(T, H, seed=12, w_dtype="f32")
+    q = synth.make(T, H, seed=13, w_dtype="f32")
+    g, h = OnGpu(p), OnGpu(q)
+    _, rstd_p = R.rmsnorm_train_fwd(g.x, g.w, p.eps)
+    _, rstd_q = R.rmsnorm_train_fwd(h.x, h.w, q.eps)
+    plan = R.rmsnorm_train_bwd_query(g.x, det)
+    assert plan.path == R.PATH_LARGE and plan.workspace_bytes > 0
+    fresh = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    dx0, dw0 = R.rmsnorm_train_bwd(g.dy, g.x, rstd_p, g.w, det, workspace=fresh)
+    nan_bytes = torch.full((plan.workspace_bytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    dx1, dw1 = R.rmsnorm_train_bwd(g.dy, g.x, rstd_p, g.w, det, workspace=nan_bytes)
+    # the same workspace, first used by a call on other inputs
+    used = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    R.rmsnorm_train_bwd(h.dy, h.x, rstd_q, h.w, det, workspace=used)
+    dx2, dw2 = R.rmsnorm_train_bwd(g.dy, g.x, rstd_p, g.w, det, workspace=used)
+    torch.cuda.synchronize()
+    for dx, dw in ((dx1, dw1), (dx2, dw2)):
+        assert np.array_equal(bits(dx), bits(dx0))
+        assert torch.equal(dw.view(torch.int32), dw0.view(torch.int32))
