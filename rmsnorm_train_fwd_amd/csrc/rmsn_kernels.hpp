@@ -26,10 +26,13 @@ __device__ __forceinline__ int64_t row_off(const RowIn& in, int64_t row, int hea
 // its row groups per workgroup are chosen on their own: one at 4096 and two at
 // 1536 and 2048 (the backward has two, four and four), which measured faster
 // than the backward's shape (e.g. the gated forward at [3534, 4096] 16.3 ->
-// 14.4 us, the plain one at [131072, 1536] 129 -> 124 us, cold caches). Other
-// widths take the backward's shape, except the gated form at 5120, which keeps
-// one 640-thread row group (8 columns per thread) where the other forms use
-// two 320-thread row groups.
+// 14.4 us, the plain one at [131072, 1536] 129 -> 124 us, cold caches); the
+// plain form at 6144 takes two 384-thread row groups of 16 columns per thread
+// ([131072, 6144] 558 -> 528 us; its residual and gated forms were slower
+// that way and keep one 768-thread row group). Other widths take the
+// backward's shape, except the gated form at 5120, which keeps one 640-thread
+// row group (8 columns per thread) where the other forms use two 320-thread
+// row groups.
 template <int H, int FORM> struct FwdCfg : Cfg<H> {};
 template <int FORM> struct FwdCfg<4096, FORM> {
   static constexpr int TPR = 512, V = 1, R = 1, D = 1;
@@ -41,6 +44,10 @@ template <int FORM> struct FwdCfg<2048, FORM> {
 };
 template <int FORM> struct FwdCfg<1536, FORM> {
   static constexpr int TPR = 192, V = 1, R = 2, D = 1;
+  static constexpr bool PIPE = true;
+};
+template <> struct FwdCfg<6144, kPlain> {
+  static constexpr int TPR = 384, V = 2, R = 2, D = 1;
   static constexpr bool PIPE = true;
 };
 template <> struct FwdCfg<5120, kGate> {
