@@ -202,7 +202,7 @@ struct RowBatch {
   __device__ __forceinline__ void compute_store(const BwdArgs& a, const float (&wr)[E],
                                                 const int64_t (&row)[D], const bool (&ok)[D],
                                                 int q, int lane, float* slots, int& parity,
-                                                Acc* acc) {
+                                                Acc* acc, bool sync = false) {
     float dot[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
@@ -248,11 +248,15 @@ struct RowBatch {
       }
     }
     RowSum<G, D>::run(dot, slots, parity, q, lane);
-    // Width 256 (half-wave row groups) has no barrier in its row sum; in the
-    // non-deterministic mode a workgroup barrier here keeps the workgroup's
-    // waves on the same tiles (measured 4-8% faster at large row counts;
-    // the deterministic mode was slower with it).
+    // Width 256 (half-wave row groups) has no barrier in its row sum; a
+    // workgroup barrier here keeps the workgroup's waves on the same tiles:
+    // measured 4-8% faster in the non-deterministic mode at large row counts,
+    // and in the deterministic mode on long chunks only (`sync`: 5-7% faster
+    // from 128 batches per chunk, slower on short ones).
     if constexpr (__is_same(Acc, Block8) && G::LANES == 32) __syncthreads();
+    if constexpr (__is_same(Acc, Dot2) && G::LANES == 32) {
+      if (sync) __syncthreads();  // uniform: one value per workgroup
+    }
     opaque();
 #pragma unroll
     for (int d = 0; d < D; ++d) {
@@ -350,7 +354,8 @@ __global__ __launch_bounds__(Geo<H>::BLOCK) void k_bwd_large(BwdArgs a) {
       int64_t row[D];
       bool ok[D];
       rows_of(b, row, ok);
-      if constexpr (DET) rb.template compute_store<WF32>(a, wr, row, ok, q, lane, slots, parity, dacc);
+      if constexpr (DET)
+        rb.template compute_store<WF32>(a, wr, row, ok, q, lane, slots, parity, dacc, nb >= 128);
       else rb.template compute_store<WF32>(a, wr, row, ok, q, lane, slots, parity, bacc);
       if constexpr (!DET) {
         if (((b + 1) * D) % 8 == 0) {
