@@ -26,6 +26,19 @@ MUTATIONS = {
     "view_head_stride_ignored": ("v->p + t * v->st + h * v->sh", "v->p + t * v->st + h * v->width"),
     "residual_not_rounded": ("h[r * n + j] = orc_f64_to_bf16(a[j] + b[j])", "h[r * n + j] = orc_f64_to_bf16(a[j])"),
     "grad_h_drops_dh": ("dxi[j] = hr[j] + dxi[j]", "dxi[j] = dxi[j]"),
+    "residual_y_from_x_not_h": ("orc_bf16_to_f64_array(h + r * n, n, a);", "load_row(x, r, a);"),
+    "residual_y_from_unrounded_sum": ("orc_bf16_to_f64_array(h + r * n, n, a);",
+                                      "load_row(x, r, a); load_row(res, r, b); "
+                                      "for (int64_t j = 0; j < n; ++j) a[j] += b[j];"),
+    "residual_sel_ignored": ("int64_t r = sel ? sel[i] : i;\n    orc_bf16_to_f64_array(h + r * n",
+                             "int64_t r = i;\n    orc_bf16_to_f64_array(h + r * n"),
+    "gate_fwd_view_z_from_x": ("load_row(z, r, zr);\n    orc_gate_fwd_f64",
+                               "load_row(x, r, zr);\n    orc_gate_fwd_f64"),
+    "gate_bwd_view_z_from_x": ("if (z) load_row(z, r, zr);", "if (z) load_row(x, r, zr);"),
+    "gate_bwd_view_dw_z_from_x": ("if (z) load_row(z, r, zr);\n      row_bwd(n, gr, xr, z ? zr : NULL, w, eps, NULL, NULL, dw);",
+                                  "if (z) load_row(x, r, zr);\n      row_bwd(n, gr, xr, z ? zr : NULL, w, eps, NULL, NULL, dw);"),
+    "gate_fwd_sel_ignored": ("int64_t r = sel ? sel[i] : i;\n    load_row(x, r, xr);\n    load_row(z, r, zr);",
+                             "int64_t r = i;\n    load_row(x, r, xr);\n    load_row(z, r, zr);"),
 }
 
 

@@ -378,3 +378,99 @@ def test_residual_backward_matches_complex_step():
     refw = _complex_step_grad(lambda c: (dy * _fwd_complex(h, c, EPS)).sum(), w)
     assert np.allclose(gh, ref, rtol=1e-12, atol=1e-14)
     assert np.allclose(dw, refw, rtol=1e-12, atol=1e-14)
+
+
+# ----------------------------------- residual forward and gated views ---
+
+def _mk_bits(rng, shape, scale=1.0):
+    a = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return _bits(torch.from_numpy(a).to(torch.bfloat16))
+
+
+def test_residual_forward_normalises_the_rounded_h():
+    # PR #8512 page, description, "Residual rows": the forward returns h = x +
+    # residual and y = RMSNorm(h); PR #8848 page, "Key": h_new = BF16(h + u).
+    # So y and rstd are the plain forward of the BF16 h the call returns.
+    # The addends are scaled so that rounding x + residual to BF16 moves each
+    # row's rstd by far more than 1e-12 relative: normalising x, or the
+    # unrounded sum, instead of h fails.
+    rng = np.random.default_rng(13)
+    T, n = 6, 64
+    xb = _mk_bits(rng, (T, n), 3.0)
+    rb = _mk_bits(rng, (T, n), 0.37)
+    w = 1 + 0.1 * rng.standard_normal(n)
+    h, y, r = oracle.res_fwd(oracle.View.dense(xb), oracle.View.dense(rb), w, EPS)
+    # the pinned plain forward, applied to the returned h
+    y2, r2 = oracle.fwd(oracle.View.dense(h), w, EPS)
+    assert np.array_equal(y, y2) and np.array_equal(r, r2)
+    # the closed form on h, evaluated here in numpy (rstd to 1e-15 relative)
+    hd = oracle.bf16_to_f64(h)
+    r_ref = 1.0 / np.sqrt((hd * hd).mean(axis=1) + EPS)
+    assert np.allclose(r, r_ref, rtol=1e-15, atol=0)
+    assert np.allclose(y, hd * r_ref[:, None] * w, rtol=1e-14, atol=0)
+    # the test inputs discriminate: rstd of the unrounded sum differs by > 1e-12
+    s = oracle.bf16_to_f64(xb) + oracle.bf16_to_f64(rb)
+    r_unrounded = 1.0 / np.sqrt((s * s).mean(axis=1) + EPS)
+    assert np.all(np.abs(r_unrounded / r_ref - 1.0) > 1e-12)
+    r_x = 1.0 / np.sqrt((oracle.bf16_to_f64(xb) ** 2).mean(axis=1) + EPS)
+    assert np.all(np.abs(r_x / r_ref - 1.0) > 1e-3)
+
+
+def test_residual_forward_row_selection_over_a_per_head_view():
+    # Rows chosen by `sel` are the same rows of the full output, in the order
+    # asked for, and h is always written for every row (strided per-head view).
+    rng = np.random.default_rng(14)
+    T, heads, n, st, sh = 4, 3, 32, 160, 48
+    xb = _mk_bits(rng, T * st)
+    rb = _mk_bits(rng, T * st)
+    w = 1 + 0.1 * rng.standard_normal(n)
+    xv = oracle.View(xb, T, heads, n, st, sh)
+    rv = oracle.View(rb, T, heads, n, st, sh)
+    h, y, r = oracle.res_fwd(xv, rv, w, EPS)
+    sel = [11, 0, 5, 5, 7]
+    hs, ys, rs = oracle.res_fwd(xv, rv, w, EPS, sel=sel)
+    assert np.array_equal(hs, h)
+    assert np.array_equal(ys, y[sel]) and np.array_equal(rs, r[sel])
+    # and the full output's rows are the rows of the view, in row order
+    for t in range(T):
+        for hh in range(heads):
+            o = t * st + hh * sh
+            ref = _bits((torch.from_numpy(oracle.bf16_to_f64(xb[o:o + n]).astype(np.float32)) +
+                         torch.from_numpy(oracle.bf16_to_f64(rb[o:o + n]).astype(np.float32)))
+                        .to(torch.bfloat16))
+            assert np.array_equal(h[t * heads + hh], ref)
+
+
+def _gather(b, T, heads, n, st, sh):
+    return np.stack([oracle.bf16_to_f64(b[t * st + h * sh: t * st + h * sh + n])
+                     for t in range(T) for h in range(heads)])
+
+
+def test_gate_view_entry_points_equal_dense_cores_with_separate_z():
+    # PR #8656 page, description: y = RMSNorm(x) w silu(z) with z its own
+    # tensor. Over a strided per-head view whose z buffer differs from x (and
+    # has its own padding), the BF16 entry points equal the pinned dense FP64
+    # cores applied to the gathered rows of x, z and dy.
+    rng = np.random.default_rng(15)
+    T, heads, n, st, sh = 5, 3, 24, 120, 40
+    xb, dyb = _mk_bits(rng, T * st), _mk_bits(rng, T * st)
+    zb = _mk_bits(rng, T * st, 2.0)
+    w = 1 + 0.1 * rng.standard_normal(n)
+    xv, zv, dyv = (oracle.View(b, T, heads, n, st, sh) for b in (xb, zb, dyb))
+    xd, zd, dyd = (_gather(b, T, heads, n, st, sh) for b in (xb, zb, dyb))
+    y, r = oracle.gate_fwd(xv, zv, w, EPS)
+    y2, r2 = oracle.gate_fwd_f64(xd, zd, w, EPS)
+    assert np.array_equal(y, y2) and np.array_equal(r, r2)
+    dx, dz, dw = oracle.gate_bwd(dyv, xv, zv, w, EPS)
+    dx2, dz2, dw2 = oracle.gate_bwd_f64(dyd, xd, zd, w, EPS)
+    assert np.array_equal(dx, dx2) and np.array_equal(dz, dz2) and np.array_equal(dw, dw2)
+    # row selection: the chosen rows of the full output; dw still over all rows
+    sel = [14, 2, 9]
+    ys, rs = oracle.gate_fwd(xv, zv, w, EPS, sel=sel)
+    assert np.array_equal(ys, y[sel]) and np.array_equal(rs, r[sel])
+    dxs, dzs, dws = oracle.gate_bwd(dyv, xv, zv, w, EPS, sel=sel)
+    assert np.array_equal(dxs, dx[sel]) and np.array_equal(dzs, dz[sel])
+    assert np.array_equal(dws, dw)
+    # the inputs discriminate: with z read through x's view the results move
+    y_xz, _ = oracle.gate_fwd_f64(xd, xd, w, EPS)
+    assert not np.allclose(y_xz, y)
