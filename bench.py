@@ -81,7 +81,7 @@ def time_calls(fn, steps, warmup, torch):
 
 def stream_ceiling(x, dy, steps, torch):
     """The practical HBM ceiling beside the kernels: the bandwidth probe
-    (librmsn_probe.so, built with the library) streams the backward's inputs
+    (probe/librmsn_probe.so, built beside the library) streams the backward's inputs
     in the same tile-dealt pattern with no arithmetic: two read + one written,
     one read + one written, read only. The output is allocated here, after the
     timed calls have freed theirs, so the caching allocator hands it the block
@@ -89,7 +89,7 @@ def stream_ceiling(x, dy, steps, torch):
     device). GB/s from the mean of HIP-event times."""
     import ctypes
 
-    path = os.path.join(ROOT, "rmsnorm_train_fwd_amd", "librmsn_probe.so")
+    path = os.path.join(ROOT, "probe", "librmsn_probe.so")
     if not os.path.exists(path):
         print("[bench] bandwidth probe not built; ceiling omitted", file=sys.stderr, flush=True)
         return None
@@ -175,7 +175,7 @@ def cpu_sweep(out_md, reps=3):
     import torch
 
     import oracle
-    from rmsnorm_train_fwd_amd import synth
+    import synth
 
     def bits(t):
         return t.contiguous().view(torch.int16).numpy().view(np.uint16)
@@ -273,7 +273,7 @@ def traffic_probe():
     import torch
 
     import rmsnorm_train_fwd_amd as R
-    from rmsnorm_train_fwd_amd import synth
+    import synth
 
     dev = torch.device("cuda:0")
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -310,7 +310,7 @@ def sweep(out_path, reps=20):
     import torch
 
     import rmsnorm_train_fwd_amd as R
-    from rmsnorm_train_fwd_amd import synth
+    import synth
 
     dev = torch.device("cuda:0")
     # Cold caches: read (not write) 512 MB between calls, evicting L2 and the
@@ -765,7 +765,7 @@ def main():
     import torch
 
     import rmsnorm_train_fwd_amd as R
-    from rmsnorm_train_fwd_amd import synth
+    import synth
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

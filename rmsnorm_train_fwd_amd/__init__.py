@@ -138,6 +138,9 @@ def _layout(x: torch.Tensor, g: Optional[torch.Tensor]) -> Layout:
 
 
 def _same_geometry(a: torch.Tensor, b: torch.Tensor, an: str, bn: str):
+    """b must be laid out like a: same shape, same token and head strides, and a
+    contiguous last dimension (the kernels read each row as 16-byte vectors)."""
+    _inner_contiguous(b, bn)
     if _geometry(a, an) != _geometry(b, bn):
         raise ValueError(f"{bn} must have the shape and strides of {an}")
 
@@ -150,6 +153,11 @@ def _w(w: torch.Tensor, width: int):
     if w.dtype == torch.float32:
         return RMSN_F32
     raise TypeError(f"w must be bfloat16 or float32, got {w.dtype}")
+
+
+def _rstd(rstd: torch.Tensor, L: Layout):
+    if rstd.dtype != torch.float32 or rstd.numel() != L.T * L.heads or not rstd.is_contiguous():
+        raise ValueError("rstd must be a contiguous float32 tensor with one value per row")
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -174,12 +182,12 @@ def rmsnorm_train_fwd(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
                       residual: Optional[torch.Tensor] = None):
     """y = RMSNorm(x) * w (BF16) and rstd (FP32). With a residual: h = x + residual
     (BF16) is normalised and returned as well: (y, rstd, h)."""
-    _on_device(x, w=w, residual=residual)
     _inner_contiguous(x, "x")
     L = _layout(x, None)
     wd = _w(w, L.width)
     if residual is not None:
         _same_geometry(x, residual, "x", "residual")
+    _on_device(x, w=w, residual=residual)
     full, rows = _rows_shape(x)
     y = torch.empty(full, dtype=torch.bfloat16, device=x.device)
     rstd = torch.empty(rows, dtype=torch.float32, device=x.device)
@@ -226,15 +234,14 @@ def rmsnorm_train_bwd(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor, w: 
                       dw_dtype: torch.dtype = torch.float32):
     """dx (BF16) and dw (FP32, or BF16 with dw_dtype=torch.bfloat16). With dh
     (residual form; x is then the forward's BF16 h): grad_h = dh + dx replaces dx."""
-    _on_device(x, dy=dy, rstd=rstd, w=w, dh=dh, workspace=workspace)
     _inner_contiguous(x, "x")
     _inner_contiguous(dy, "dy")
     L = _layout(x, dy)
     wd = _w(w, L.width)
     if dh is not None:
         _same_geometry(dy, dh, "dy", "dh")
-    if rstd.dtype != torch.float32 or rstd.numel() != L.T * L.heads or not rstd.is_contiguous():
-        raise ValueError("rstd must be a contiguous float32 tensor with one value per row")
+    _rstd(rstd, L)
+    _on_device(x, dy=dy, rstd=rstd, w=w, dh=dh, workspace=workspace)
     plan = rmsnorm_train_bwd_query(x, deterministic, launch, dy)
     ws, ws_bytes = _workspace(plan, x, workspace)
     full, _ = _rows_shape(x)
@@ -252,11 +259,11 @@ def rmsnorm_train_bwd(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor, w: 
 def rmsnorm_silu_gate_train_fwd(x: torch.Tensor, z: torch.Tensor, w: torch.Tensor,
                                 eps: float = 1e-6):
     """y = RMSNorm(x) * w * silu(z) (BF16) and rstd (FP32)."""
-    _on_device(x, z=z, w=w)
     _inner_contiguous(x, "x")
     _same_geometry(x, z, "x", "z")
     L = _layout(x, None)
     wd = _w(w, L.width)
+    _on_device(x, z=z, w=w)
     full, rows = _rows_shape(x)
     y = torch.empty(full, dtype=torch.bfloat16, device=x.device)
     rstd = torch.empty(rows, dtype=torch.float32, device=x.device)
@@ -274,14 +281,13 @@ def rmsnorm_silu_gate_train_bwd(dy: torch.Tensor, x: torch.Tensor, z: torch.Tens
                                 dw_dtype: torch.dtype = torch.float32):
     """dx, dz (BF16) and dw (FP32, or BF16 with dw_dtype=torch.bfloat16) of the
     SiLU-gated form."""
-    _on_device(x, dy=dy, z=z, rstd=rstd, w=w, workspace=workspace)
     _inner_contiguous(x, "x")
     _inner_contiguous(dy, "dy")
     _same_geometry(x, z, "x", "z")
     L = _layout(x, dy)
     wd = _w(w, L.width)
-    if rstd.dtype != torch.float32 or rstd.numel() != L.T * L.heads or not rstd.is_contiguous():
-        raise ValueError("rstd must be a contiguous float32 tensor with one value per row")
+    _rstd(rstd, L)
+    _on_device(x, dy=dy, z=z, rstd=rstd, w=w, workspace=workspace)
     plan = rmsnorm_train_bwd_query(x, deterministic, launch, dy)
     ws, ws_bytes = _workspace(plan, x, workspace)
     full, _ = _rows_shape(x)

@@ -1,5 +1,4 @@
-"""Build the gfx950 HIP library librmsnorm_train.so in-tree with hipcc, and the
-bandwidth probe librmsn_probe.so that only the benchmark loads.
+"""Build the gfx950 HIP library librmsnorm_train.so in-tree with hipcc.
 
 Flags that matter for correctness:
   -ffp-contract=off      keep every FP32 rounding where the source writes it
@@ -18,8 +17,6 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "librmsnorm_train.so")
 BUILD = os.path.join(PKG, "_build")
 SOURCES = ["rmsn_abi.cpp", "rmsn_fwd.hip", "rmsn_bwd_large.hip", "rmsn_bwd_small.hip"]
-PROBE_SRC = os.path.join("probe", "rmsn_stream_probe.hip")
-PROBE_LIB = os.path.join(PKG, "librmsn_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
@@ -48,15 +45,14 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES) + 1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)))
+    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES + [PROBE_SRC]))
-    for lib, lib_objs in ((LIB, objs[:-1]), (PROBE_LIB, objs[-1:])):
-        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib + ".tmp", *lib_objs]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
-        os.replace(lib + ".tmp", lib)
+        objs = list(ex.map(_compile, SOURCES))
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
     return LIB
 
 

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import rmsnorm_train_fwd_amd as R
-from rmsnorm_train_fwd_amd import synth
+import synth
 
 TOL_DX = (1e-2, 1e-2)
 TOL_DW = (1e-4, 1e-4)

@@ -239,7 +239,7 @@ def test_bandwidth_probe_library_loads_and_rejects_bad_arguments():
     # The probe that bench.py times beside the kernels (a separate library, not
     # part of the normalisation ABI). Only argument errors are exercised here:
     # they return before any HIP call, so nothing launches.
-    path = os.path.join(os.path.dirname(R.__file__), "librmsn_probe.so")
+    path = os.path.join(ROOT, "probe", "librmsn_probe.so")
     f = C.CDLL(path).rmsn_stream_probe
     f.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int,
                   C.c_void_p]

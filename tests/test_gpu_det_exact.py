@@ -22,7 +22,7 @@ import torch
 
 import oracle
 import rmsnorm_train_fwd_amd as R
-from rmsnorm_train_fwd_amd import synth
+import synth
 
 from helpers import OnGpu, oview, w_f64
 

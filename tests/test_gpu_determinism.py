@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import rmsnorm_train_fwd_amd as R
-from rmsnorm_train_fwd_amd import synth
+import synth
 
 from helpers import OnGpu, bits
 

@@ -28,7 +28,7 @@ import torch
 
 import oracle
 import rmsnorm_train_fwd_amd as R
-from rmsnorm_train_fwd_amd import synth
+import synth
 
 from helpers import TOL_DW, TOL_DX, TOL_Y, RTOL_RSTD, assert_within, bits, w_f64
 

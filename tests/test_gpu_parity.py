@@ -7,15 +7,13 @@ synth.py): [8,512] fwd+bwd; the small-row deterministic sweep incl. per-head
 [T,24,256] views; large-T non-deterministic and deterministic backward;
 fused residual at width 6144; the SiLU gate at width 4096.
 """
-import os
-
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import rmsnorm_train_fwd_amd as R
-from rmsnorm_train_fwd_amd import synth
+import synth
 
 from helpers import (TOL_DW, TOL_DX, TOL_Y, RTOL_RSTD, OnGpu, assert_within, bf16_ulp_distance,
                      bits, oview, ratio, sample_rows, w_f64)
@@ -24,22 +22,28 @@ pytestmark = pytest.mark.gpu
 
 WIDTHS = (512, 1536, 2048, 4096, 5120, 6144)
 SMALL_T = (1, 2, 4, 8, 16, 32, 64, 128, 203)
-FULL = os.environ.get("RMSN_FULL") == "1"
 
 
 def run_case(p: synth.Problem, det=True, form="plain", launch=None, nsample=None, seed=0):
-    """fwd + bwd on the GPU, checked against the oracle. Returns error ratios."""
+    """fwd + bwd on the GPU, checked against the oracle. `det` is one mode or a
+    tuple of modes: the forward and the oracle run once and every mode's
+    backward is checked against them. Returns error ratios (of the last mode)."""
+    modes = tuple(det) if isinstance(det, (tuple, list)) else (det,)
     g = OnGpu(p)
+    bwd_out = {}
     if form == "residual":
         y, rstd, h = R.rmsnorm_train_fwd(g.x, g.w, p.eps, residual=g.e)
-        xin = h
-        dx, dw = R.rmsnorm_train_bwd(g.dy, h, rstd, g.w, det, dh=g.dh, launch=launch)
+        for m in modes:
+            bwd_out[m] = R.rmsnorm_train_bwd(g.dy, h, rstd, g.w, m, dh=g.dh, launch=launch) + (None,)
     elif form == "gate":
         y, rstd = R.rmsnorm_silu_gate_train_fwd(g.x, g.e, g.w, p.eps)
-        dx, dz, dw = R.rmsnorm_silu_gate_train_bwd(g.dy, g.x, g.e, rstd, g.w, det, launch=launch)
+        for m in modes:
+            dx, dz, dw = R.rmsnorm_silu_gate_train_bwd(g.dy, g.x, g.e, rstd, g.w, m, launch=launch)
+            bwd_out[m] = (dx, dw, dz)
     else:
         y, rstd = R.rmsnorm_train_fwd(g.x, g.w, p.eps)
-        dx, dw = R.rmsnorm_train_bwd(g.dy, g.x, rstd, g.w, det, launch=launch)
+        for m in modes:
+            bwd_out[m] = R.rmsnorm_train_bwd(g.dy, g.x, rstd, g.w, m, launch=launch) + (None,)
     torch.cuda.synchronize()
 
     rows, W = p.rows, p.width
@@ -57,8 +61,6 @@ def run_case(p: synth.Problem, det=True, form="plain", launch=None, nsample=None
         zo = oview(p, p.extra)
         yo, ro = oracle.gate_fwd(xo, zo, w64, p.eps, sel)
         rows_out, dzo, dwo = oracle.gate_bwd(dyo, xo, zo, w64, p.eps, sel)
-        dzg = oracle.bf16_to_f64(bits(dz).reshape(rows, W)[sel])
-        out["dz"] = assert_within(dzg, dzo, TOL_DX, "dz")
     else:
         yo, ro = oracle.fwd(xo, w64, p.eps, sel)
         rows_out, dwo = oracle.bwd(dyo, xo, w64, p.eps, sel=sel)
@@ -69,9 +71,16 @@ def run_case(p: synth.Problem, det=True, form="plain", launch=None, nsample=None
     assert ulp.max(initial=0) <= 1, f"y differs from the rounded oracle by {ulp.max()} BF16 ulp"
     rg = rstd.reshape(-1).cpu().double().numpy()[sel]
     out["rstd"] = assert_within(rg, ro, (0.0, RTOL_RSTD), "rstd")
-    dxg = oracle.bf16_to_f64(bits(dx).reshape(rows, W)[sel])
-    out["dx"] = assert_within(dxg, rows_out, TOL_DX, "dx" if form != "residual" else "grad_h")
-    out["dw"] = assert_within(dw.cpu().double().numpy(), dwo, TOL_DW, "dw")
+    for m in modes:
+        dx, dw, dz = bwd_out[m]
+        tag = "det" if m else "nondet"
+        if form == "gate":
+            dzg = oracle.bf16_to_f64(bits(dz).reshape(rows, W)[sel])
+            out["dz"] = assert_within(dzg, dzo, TOL_DX, f"dz ({tag})")
+        dxg = oracle.bf16_to_f64(bits(dx).reshape(rows, W)[sel])
+        out["dx"] = assert_within(dxg, rows_out, TOL_DX,
+                                  f"{'dx' if form != 'residual' else 'grad_h'} ({tag})")
+        out["dw"] = assert_within(dw.cpu().double().numpy(), dwo, TOL_DW, f"dw ({tag})")
     return out
 
 
@@ -125,12 +134,13 @@ def test_config3_full_size_nondet(T, H):
     run_case(synth.make(T, H, seed=2, w_dtype="f32"), det=False, nsample=32)
 
 
-@pytest.mark.skipif(not FULL, reason="full config-3 sweep: set RMSN_FULL=1")
-@pytest.mark.parametrize("det", [False, True], ids=["nondet", "det"])
 @pytest.mark.parametrize("T", [65537, 98304, 131072])
 @pytest.mark.parametrize("H", (1536, 2048, 4096, 5120, 6144))
-def test_config3_full_sweep(H, T, det):
-    run_case(synth.make(T, H, seed=3, w_dtype="f32"), det=det, nsample=24)
+def test_config3_full_sweep(H, T):
+    # every config-3 shape in both modes (PR #8848 page, "Measurement": every
+    # row of the table runs both); sampled rows, dw on every column
+    print(f"[config3] [{T}, {H}] non-det + det", flush=True)
+    run_case(synth.make(T, H, seed=3, w_dtype="f32"), det=(False, True), nsample=24)
 
 
 # ------------------------------------------------------------- config 4 ---
@@ -145,10 +155,11 @@ def test_config4_residual_6144(w_dtype, det):
              form="residual", nsample=32)
 
 
-@pytest.mark.skipif(not FULL, reason="T=131072 residual: set RMSN_FULL=1")
-def test_config4_residual_131072():
-    run_case(synth.make(131072, 6144, seed=1, w_dtype="f32", form="residual"), det=True,
-             form="residual", nsample=24)
+@pytest.mark.parametrize("w_dtype", ["f32", "bf16"])
+def test_config4_residual_131072(w_dtype):
+    print(f"[config4] residual [131072, 6144] w {w_dtype}, non-det + det", flush=True)
+    run_case(synth.make(131072, 6144, seed=1, w_dtype=w_dtype, form="residual"),
+             det=(False, True), form="residual", nsample=24)
 
 
 # ------------------------------------------------------------- config 5 ---

@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import rmsnorm_train_fwd_amd as R
-from rmsnorm_train_fwd_amd import synth
+import synth
 
 from helpers import OnGpu, bits, oview, w_f64
 

@@ -344,7 +344,7 @@ def test_plain_fp32_column_sum_fails_budget_on_cancellation_family():
     # FP64) must reject a plain sequential FP32 column sum on the cancellation
     # family, while the FP64 oracle sits far inside it (review on the PR #8512
     # page asks for exactly this check).
-    from rmsnorm_train_fwd_amd import synth
+    import synth
 
     p = synth.make(8192, 512, seed=0, family="cancel", w_dtype="f32")
     xb = _bits(p.x).reshape(p.T, p.width)
