@@ -53,8 +53,11 @@
  *  - Overlap: no output may share a byte with an input or another output
  *    (extents are [base, base + last element]); dw never overlaps w ([F]).
  *  - Errors: every check runs before anything is enqueued; on error nothing is
- *    launched and no output is touched. RMSN_E_HIP means a launch failed after
- *    validation (outputs then undefined).
+ *    launched and no output is touched. RMSN_E_HIP means that the HIP runtime
+ *    refused one of this call's own launches after validation (outputs then
+ *    undefined). The library never reads or clears the calling thread's HIP
+ *    last-error state (hipGetLastError), so an earlier, unrelated error stays
+ *    the caller's to see and does not turn a good call into RMSN_E_HIP.
  *  - T == 0 is valid: the forward enqueues nothing; the backward writes
  *    dw = 0. Row pointers may then be NULL.
  */

@@ -46,9 +46,9 @@ __global__ __launch_bounds__(kFoldThreads) void k_fold(const double* __restrict_
 namespace {
 template <int H, bool WF32, int FORM>
 hipError_t large_mode(bool det, const BwdArgs& a, int grid, hipStream_t s) {
-  if (det) k_bwd_large<H, WF32, FORM, true, BwdShape<H, FORM>::D><<<grid, Geo<H>::BLOCK, 0, s>>>(a);
-  else k_bwd_large<H, WF32, FORM, false, BwdShape<H, FORM>::D><<<grid, Geo<H>::BLOCK, 0, s>>>(a);
-  return hipGetLastError();
+  constexpr int D = BwdShape<H, FORM>::D;
+  if (det) return launch_kernel(k_bwd_large<H, WF32, FORM, true, D>, grid, Geo<H>::BLOCK, s, a);
+  return launch_kernel(k_bwd_large<H, WF32, FORM, false, D>, grid, Geo<H>::BLOCK, s, a);
 }
 
 template <int H, bool WF32>
@@ -83,8 +83,7 @@ hipError_t launch_bwd_large(int H, bool w_f32, int form, bool det, const BwdArgs
 }
 
 hipError_t launch_fold(int H, const BwdArgs& a, int grid, hipStream_t s) {
-  k_fold<<<grid, kFoldThreads, 0, s>>>(a.ws, a.dw, a.dw_bf16, H, a.chunks);
-  return hipGetLastError();
+  return launch_kernel(k_fold, grid, kFoldThreads, s, a.ws, a.dw, a.dw_bf16, H, a.chunks);
 }
 
 }  // namespace rmsn

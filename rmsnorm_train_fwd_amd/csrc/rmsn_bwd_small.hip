@@ -7,13 +7,13 @@ namespace {
 template <int H, bool WF32>
 hipError_t small_form(int form, const BwdArgs& a, int row_grid, int col_grid, hipStream_t s) {
   const int grid = row_grid + col_grid;
+  constexpr int B = SmallGeo<H>::BLOCK;
   switch (form) {
-    case kPlain: k_bwd_small<H, WF32, kPlain><<<grid, SmallGeo<H>::BLOCK, 0, s>>>(a, row_grid); break;
-    case kResidual: k_bwd_small<H, WF32, kResidual><<<grid, SmallGeo<H>::BLOCK, 0, s>>>(a, row_grid); break;
-    case kGate: k_bwd_small<H, WF32, kGate><<<grid, SmallGeo<H>::BLOCK, 0, s>>>(a, row_grid); break;
+    case kPlain: return launch_kernel(k_bwd_small<H, WF32, kPlain>, grid, B, s, a, row_grid);
+    case kResidual: return launch_kernel(k_bwd_small<H, WF32, kResidual>, grid, B, s, a, row_grid);
+    case kGate: return launch_kernel(k_bwd_small<H, WF32, kGate>, grid, B, s, a, row_grid);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 template <int H>

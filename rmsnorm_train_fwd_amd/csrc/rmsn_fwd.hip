@@ -9,14 +9,15 @@ constexpr int kFwdRPG = 2;  // rows per row group per tile
 template <int H, bool WF32>
 hipError_t fwd_form(int form, const FwdArgs& a, int grid, hipStream_t s) {
   switch (form) {
-    case kPlain: k_fwd<H, WF32, kPlain, kFwdRPG><<<grid, FGeo<H, kPlain>::BLOCK, 0, s>>>(a); break;
+    case kPlain:
+      return launch_kernel(k_fwd<H, WF32, kPlain, kFwdRPG>, grid, FGeo<H, kPlain>::BLOCK, s, a);
     case kResidual:
-      k_fwd<H, WF32, kResidual, kFwdRPG><<<grid, FGeo<H, kResidual>::BLOCK, 0, s>>>(a);
-      break;
-    case kGate: k_fwd<H, WF32, kGate, kFwdRPG><<<grid, FGeo<H, kGate>::BLOCK, 0, s>>>(a); break;
+      return launch_kernel(k_fwd<H, WF32, kResidual, kFwdRPG>, grid, FGeo<H, kResidual>::BLOCK, s,
+                           a);
+    case kGate:
+      return launch_kernel(k_fwd<H, WF32, kGate, kFwdRPG>, grid, FGeo<H, kGate>::BLOCK, s, a);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 template <int H>

@@ -11,10 +11,31 @@
 // slice it needs in registers for its whole lifetime.
 #pragma once
 
+#include <tuple>
+
 #include "rmsn_device.hpp"
 #include "rmsn_launch.hpp"
 
 namespace rmsn {
+
+// Enqueues k<<<grid, block, 0, s>>>(a...) through hipLaunchKernel and returns
+// that launch's own status. A triple-chevron launch reports only through the
+// thread's last-error state, which can hold an earlier, unrelated error (and
+// reading it with hipGetLastError would clear it for the caller), so the
+// library never reads or clears that state. Each argument is converted to the
+// kernel's parameter type before its address is passed.
+template <class... P, class... A>
+hipError_t launch_kernel(void (*k)(P...), int grid, int block, hipStream_t s, A... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "one argument per kernel parameter");
+  std::tuple<P...> v(a...);
+  return std::apply(
+      [&](P&... p) {
+        void* args[] = {static_cast<void*>(&p)...};
+        return hipLaunchKernel(reinterpret_cast<const void*>(k), dim3(grid), dim3(block), args,
+                               0, s);
+      },
+      v);
+}
 
 __device__ __forceinline__ int64_t row_off(const RowIn& in, int64_t row, int heads) {
   const uint32_t t = (uint32_t)row / (uint32_t)heads;

@@ -43,8 +43,9 @@ struct BwdArgs {
   int32_t heads;
 };
 
-// Each returns hipGetLastError() after enqueueing (hipErrorInvalidValue for a
-// width / form combination that has no kernel).
+// Each returns the status of its own launches (hipLaunchKernel's result;
+// hipErrorInvalidValue for a width / form combination that has no kernel) and
+// leaves the thread's last-error state alone.
 hipError_t launch_fwd(int H, bool w_f32, int form, const FwdArgs& a, int grid, hipStream_t s);
 hipError_t launch_bwd_large(int H, bool w_f32, int form, bool det, const BwdArgs& a, int grid,
                             hipStream_t s);
