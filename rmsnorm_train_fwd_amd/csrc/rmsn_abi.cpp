@@ -6,9 +6,8 @@
 #include <math.h>
 #include <string.h>
 
+#include "rmsn_abi_internal.hpp"
 #include "rmsn_launch.hpp"
-
-#define RMSN_API extern "C" __attribute__((visibility("default")))
 
 namespace {
 
@@ -161,11 +160,16 @@ RowIn row_in(const void* p, int64_t st, int64_t sh) {
   return RowIn{static_cast<const uint16_t*>(p), st, sh};
 }
 
+}  // namespace
+
+namespace rmsn {
+
 // ---------------------------------------------------------------- backward --
 rmsn_status bwd_common(int form, const void* dy, const void* x, const void* e, const void* w,
-                       rmsn_dtype w_dtype, const float* rstd, int det, const rmsn_layout* L,
-                       void* dx, void* dz, void* dw, rmsn_dtype dw_dtype, void* ws,
-                       size_t ws_bytes, const rmsn_launch* o, void* stream) {
+                       int w_dtype, const float* rstd, int det, const rmsn_layout* L,
+                       void* dx, void* dz, void* dw, int dw_dtype, void* ws,
+                       size_t ws_bytes, WorkspaceSource ws_source, const rmsn_launch* o,
+                       void* stream) {
   rmsn_status st = check_layout(L);
   if (st) return st;
   if (w_dtype != RMSN_BF16 && w_dtype != RMSN_F32) return RMSN_E_DTYPE;
@@ -185,6 +189,9 @@ rmsn_status bwd_common(int form, const void* dy, const void* x, const void* e, c
   }
   rmsn_bwd_plan plan;
   make_plan(*L, det, o, &plan);
+  if (ws_source && plan.workspace_bytes > 0) {
+    if ((st = ws_source(plan.workspace_bytes, &ws, &ws_bytes))) return st;
+  }
   if (plan.workspace_bytes > 0) {
     if (!ws || ws_bytes < plan.workspace_bytes) return RMSN_E_WORKSPACE;
     if (!aligned(ws, 16)) return RMSN_E_ALIGN;
@@ -240,12 +247,14 @@ rmsn_status bwd_common(int form, const void* dy, const void* x, const void* e, c
   return err == hipSuccess ? RMSN_OK : RMSN_E_HIP;
 }
 
-}  // namespace
+}  // namespace rmsn
+
+using rmsn::bwd_common;
 
 // ================================================================ C ABI ====
 
 RMSN_API const char* rmsn_status_str(rmsn_status s) {
-  switch (s) {
+  switch (enum_code(s)) {
     case RMSN_OK: return "ok";
     case RMSN_E_NULL: return "a required pointer is NULL";
     case RMSN_E_DTYPE: return "unsupported dtype";
@@ -273,7 +282,7 @@ RMSN_API rmsn_status rmsnorm_train_bwd_query(const rmsn_layout* L, int determini
 }
 
 static rmsn_status fwd_common(int form, const void* x, const void* e, const void* w,
-                              rmsn_dtype w_dtype, float eps, const rmsn_layout* L, void* y,
+                              int w_dtype, float eps, const rmsn_layout* L, void* y,
                               void* h_out, float* rstd, void* stream) {
   rmsn_status st = check_layout(L);
   if (st) return st;
@@ -325,15 +334,15 @@ static rmsn_status fwd_common(int form, const void* x, const void* e, const void
 RMSN_API rmsn_status rmsnorm_train_fwd(const void* x, const void* residual, const void* w,
                                        rmsn_dtype w_dtype, float eps, const rmsn_layout* L,
                                        void* y, void* h_out, float* rstd, void* stream) {
-  return fwd_common(residual ? kResidual : kPlain, x, residual, w, w_dtype, eps, L, y, h_out,
-                    rstd, stream);
+  return fwd_common(residual ? kResidual : kPlain, x, residual, w, enum_code(w_dtype), eps, L, y,
+                    h_out, rstd, stream);
 }
 
 RMSN_API rmsn_status rmsnorm_silu_gate_train_fwd(const void* x, const void* z, const void* w,
                                                  rmsn_dtype w_dtype, float eps,
                                                  const rmsn_layout* L, void* y, float* rstd,
                                                  void* stream) {
-  return fwd_common(kGate, x, z, w, w_dtype, eps, L, y, nullptr, rstd, stream);
+  return fwd_common(kGate, x, z, w, enum_code(w_dtype), eps, L, y, nullptr, rstd, stream);
 }
 
 RMSN_API rmsn_status rmsnorm_train_bwd(const void* dy, const void* x, const void* dh,
@@ -342,8 +351,9 @@ RMSN_API rmsn_status rmsnorm_train_bwd(const void* dy, const void* x, const void
                                        void* dw, rmsn_dtype dw_dtype, void* workspace,
                                        size_t workspace_bytes, const rmsn_launch* launch,
                                        void* stream) {
-  return bwd_common(dh ? kResidual : kPlain, dy, x, dh, w, w_dtype, rstd, deterministic, L, dx,
-                    nullptr, dw, dw_dtype, workspace, workspace_bytes, launch, stream);
+  return bwd_common(dh ? kResidual : kPlain, dy, x, dh, w, enum_code(w_dtype), rstd,
+                    deterministic, L, dx, nullptr, dw, enum_code(dw_dtype), workspace,
+                    workspace_bytes, nullptr, launch, stream);
 }
 
 RMSN_API rmsn_status rmsnorm_silu_gate_train_bwd(const void* dy, const void* x, const void* z,
@@ -353,6 +363,6 @@ RMSN_API rmsn_status rmsnorm_silu_gate_train_bwd(const void* dy, const void* x, 
                                                  void* dw, rmsn_dtype dw_dtype, void* workspace,
                                                  size_t workspace_bytes,
                                                  const rmsn_launch* launch, void* stream) {
-  return bwd_common(kGate, dy, x, z, w, w_dtype, rstd, deterministic, L, dx, dz, dw, dw_dtype,
-                    workspace, workspace_bytes, launch, stream);
+  return bwd_common(kGate, dy, x, z, w, enum_code(w_dtype), rstd, deterministic, L, dx, dz, dw,
+                    enum_code(dw_dtype), workspace, workspace_bytes, nullptr, launch, stream);
 }
