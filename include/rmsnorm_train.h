@@ -170,6 +170,27 @@ rmsn_status rmsnorm_train_bwd(const void* dy, const void* x, const void* dh, con
                               void* workspace, size_t workspace_bytes, const rmsn_launch* launch,
                               void* stream);
 
+/* ------------------------------------------------- backward, no allocation --
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the call
+ * rmsnorm_train_bwd makes (same forms, modes, kernels and results, bit for
+ * bit), without the workspace arguments. Its workspace is a device array
+ * inside the library, 12 MiB per GPU (256 chunks x 6144 columns of FP64, the
+ * largest any plan needs), held by each GPU the library runs on until the
+ * process ends; a plan needing more would return RMSN_E_WORKSPACE. The call
+ * uses the array of the calling thread's current HIP device, so `stream` must
+ * belong to that device; the first call on a device looks up the array's
+ * address there (RMSN_E_HIP if that fails). It calls no allocator.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (nothing in it needs clearing). Calls that can overlap in time on
+ * one GPU (unordered streams, several host threads) race on the array and
+ * must not be made; calls ordered on one stream are safe.                   */
+rmsn_status rmsnorm_train_bwd_noalloc(const void* dy, const void* x, const void* dh,
+                                      const void* w, rmsn_dtype w_dtype, const float* rstd,
+                                      int deterministic, const rmsn_layout* L, void* dx,
+                                      void* dw, rmsn_dtype dw_dtype, const rmsn_launch* launch,
+                                      void* stream);
+
 /* Host-only: the plan (path, chunking, grids, workspace bytes) of a backward
  * call with this layout, mode and override. Validates L and the override.   */
 rmsn_status rmsnorm_train_bwd_query(const rmsn_layout* L, int deterministic,

@@ -11,6 +11,8 @@ Names follow the C ABI:
   rmsnorm_train_bwd_query(shape..., deterministic)   -> plan (host only)
   rmsnorm_silu_gate_train_fwd(x, z, w, eps)          -> y, rstd
   rmsnorm_silu_gate_train_bwd(dy, x, z, rstd, w, deterministic) -> dx, dz, dw
+  rmsnorm_train_bwd_noalloc(dy, x, rstd, w, deterministic, dh=None) -> dx | grad_h, dw
+    (the library's workspace-free backward; this binding still allocates the outputs)
 Row tensors are BF16 [T, H] (one row per token) or [T, heads, width] views
 whose last dimension is contiguous; w is [width] BF16 or FP32.
 """
@@ -34,7 +36,8 @@ STATUS = {
 }
 EXPORTS = (
     "rmsnorm_train_fwd", "rmsnorm_train_bwd", "rmsnorm_train_bwd_query",
-    "rmsnorm_silu_gate_train_fwd", "rmsnorm_silu_gate_train_bwd", "rmsn_status_str",
+    "rmsnorm_silu_gate_train_fwd", "rmsnorm_silu_gate_train_bwd", "rmsnorm_train_bwd_noalloc",
+    "rmsn_status_str",
 )
 
 
@@ -81,6 +84,8 @@ def lib():
         L.rmsnorm_silu_gate_train_fwd.argtypes = [vp, vp, vp, C.c_int, fp, lp, vp, vp, vp]
         L.rmsnorm_silu_gate_train_bwd.argtypes = [vp, vp, vp, vp, C.c_int, vp, C.c_int, lp, vp,
                                                   vp, vp, C.c_int, vp, C.c_size_t, lap, vp]
+        L.rmsnorm_train_bwd_noalloc.argtypes = [vp, vp, vp, vp, C.c_int, vp, C.c_int, lp, vp, vp,
+                                                C.c_int, lap, vp]
         for name in EXPORTS[:-1]:
             getattr(L, name).restype = C.c_int
         L.rmsn_status_str.argtypes = [C.c_int]
@@ -302,3 +307,31 @@ def rmsnorm_silu_gate_train_bwd(dy: torch.Tensor, x: torch.Tensor, z: torch.Tens
                                                  _stream(x)),
                "rmsnorm_silu_gate_train_bwd")
     return dx, dz, dw
+
+
+def rmsnorm_train_bwd_noalloc(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor,
+                              w: torch.Tensor, deterministic: bool = True,
+                              dh: Optional[torch.Tensor] = None, launch: Optional[Launch] = None,
+                              dw_dtype: torch.dtype = torch.float32):
+    """rmsnorm_train_bwd through the library's workspace-free entry point (its
+    workspace is a device array inside the library, shared by every call on a
+    GPU: calls that can overlap in time on one GPU race). Same results, bit for
+    bit. Only the outputs are allocated here."""
+    _inner_contiguous(x, "x")
+    _inner_contiguous(dy, "dy")
+    L = _layout(x, dy)
+    wd = _w(w, L.width)
+    if dh is not None:
+        _same_geometry(dy, dh, "dy", "dh")
+    _rstd(rstd, L)
+    _on_device(x, dy=dy, rstd=rstd, w=w, dh=dh)
+    full, _ = _rows_shape(x)
+    dx = torch.empty(full, dtype=torch.bfloat16, device=x.device)
+    dw, dwd = _dw(L.width, dw_dtype, x.device)
+    with torch.cuda.device(x.device):
+        _check(lib().rmsnorm_train_bwd_noalloc(_ptr(dy), _ptr(x), _ptr(dh), _ptr(w), wd,
+                                               _ptr(rstd), int(bool(deterministic)), C.byref(L),
+                                               _ptr(dx), _ptr(dw), dwd,
+                                               C.byref(launch) if launch else None, _stream(x)),
+               "rmsnorm_train_bwd_noalloc")
+    return dx, dw

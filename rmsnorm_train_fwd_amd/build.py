@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "librmsnorm_train.so")
 BUILD = os.path.join(PKG, "_build")
-SOURCES = ["rmsn_abi.cpp", "rmsn_fwd.hip", "rmsn_bwd_large.hip", "rmsn_bwd_small.hip"]
+SOURCES = ["rmsn_abi.cpp", "rmsn_fwd.hip", "rmsn_bwd_large.hip", "rmsn_bwd_small.hip",
+           "rmsn_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
