@@ -121,7 +121,14 @@ def stream_ceiling(x, dy, steps, torch):
 
 
 def cpu_baseline(p, rows_sample, reps=3):
-    """The FP64 oracle (single-threaded C) on the workload's rows: median of reps."""
+    """The FP64 oracle (plain C, unchanged) on the workload's rows, median of
+    reps: once on one thread, and once on every core this process may use, the
+    rows cut into one fixed block per core, each block a concurrent call of the
+    same single-threaded oracle (ctypes releases the GIL for the call), and the
+    blocks' dw added in block order. The single-threaded call stays the
+    checker; the blocked run only times the oracle on all cores."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import torch
 
@@ -131,25 +138,54 @@ def cpu_baseline(p, rows_sample, reps=3):
     xs = p.x.view(-1, W)[:rows_sample].contiguous().view(torch.int16).numpy().view(np.uint16)
     dys = p.dy.view(-1, W)[:rows_sample].contiguous().view(torch.int16).numpy().view(np.uint16)
     w64 = p.w.double().numpy()
-    times = []
-    for _ in range(reps):
-        t0 = time.perf_counter()
+    host = host_cpu()
+    cores = host["cpus_available"]
+    bounds = [rows_sample * i // cores for i in range(cores + 1)]
+    oracle.lib()  # load (and, if stale, build) the library before anything is timed
+
+    def one_thread():
         oracle.bwd(oracle.View.dense(dys), oracle.View.dense(xs), w64, p.eps)
-        times.append(time.perf_counter() - t0)
-    dt = sorted(times)[len(times) // 2]
-    gbps = bwd_bytes(rows_sample, W, 4) / dt / 1e9
+
+    def block(i):
+        a, b = bounds[i], bounds[i + 1]
+        return oracle.bwd(oracle.View.dense(dys[a:b]), oracle.View.dense(xs[a:b]), w64, p.eps)
+
+    def all_cores(ex):
+        dw = np.zeros(W)
+        for _, dwb in ex.map(block, range(cores)):
+            dw = dw + dwb
+        return dw
+
+    def med_time(fn):
+        times = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            times.append(time.perf_counter() - t0)
+        return sorted(times)[len(times) // 2]
+
+    dt1 = med_time(one_thread)
+    with ThreadPoolExecutor(cores) as ex:
+        dtn = med_time(lambda: all_cores(ex))
+    nbytes = bwd_bytes(rows_sample, W, 4)
+    scale = p.T / rows_sample
     return {
-        "value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "value": round(nbytes / dtn / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
         "sample": f"backward (dx for every row, dw over every row) of {rows_sample} of {p.T} "
-                  f"rows, width {W}, FP64 C oracle, median of {reps} runs ({dt:.2f} s each); "
-                  "same algorithmic byte model as value",
-        "us_per_call": round(dt * 1e6 * p.T / rows_sample, 1),
-        "host": host_cpu(),
+                  f"rows, width {W}, FP64 C oracle unchanged: {cores} concurrent calls on fixed "
+                  f"row blocks (dw added in block order), median of {reps} runs ({dtn:.2f} s "
+                  "each); same algorithmic byte model as value",
+        "us_per_call": round(dtn * 1e6 * scale, 1),
+        "single_thread": {"value": round(nbytes / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                          "us_per_call": round(dt1 * 1e6 * scale, 1),
+                          "sample": f"the same rows in one call, median of {reps} runs "
+                                    f"({dt1:.2f} s each)"},
+        "host": host,
     }
 
 
 def host_cpu():
-    """CPU model and the logical CPUs this process may run on (the oracle uses one)."""
+    """CPU model (lscpu, else /proc/cpuinfo) and the logical CPUs this process may run on."""
     model = "unknown"
     try:
         with open("/proc/cpuinfo") as fh:
@@ -159,11 +195,24 @@ def host_cpu():
                     break
     except OSError:
         pass
+    lscpu = {}
+    try:
+        import subprocess
+
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            k, _, v = line.partition(":")
+            if k.strip() in ("Model name", "Vendor ID", "CPU(s)", "Thread(s) per core",
+                             "Core(s) per socket", "Socket(s)", "NUMA node(s)", "CPU max MHz",
+                             "L3 cache", "Hypervisor vendor", "Virtualization type"):
+                lscpu[k.strip()] = v.strip()
+    except (OSError, ValueError, subprocess.SubprocessError):
+        pass
     try:
         avail = len(os.sched_getaffinity(0))
     except (AttributeError, OSError):
         avail = os.cpu_count()
-    return {"model": model, "cpus_available": avail}
+    return {"model": lscpu.get("Model name", model), "cpus_available": avail, "lscpu": lscpu}
 
 
 def cpu_sweep(out_md, reps=3):
@@ -716,6 +765,80 @@ x, dy and dx are each moved once. Kernel sources hash: {out['kernel_hash']} (ben
     print(md)
 
 
+def headline_setup():
+    """Inputs of the headline workload on cuda:0, its forward's rstd and the
+    backward workspace: (problem, x, dy, w, rstd, workspace, plan, y). The
+    forward's y stays allocated for the caller, so the timed calls' dx lands
+    where it always has relative to x and dy (placement moves this call)."""
+    import torch
+
+    import rmsnorm_train_fwd_amd as R
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating inputs [{T_HEAD}, {H_HEAD}]", file=sys.stderr, flush=True)
+    p = synth.make(T_HEAD, H_HEAD, seed=0, w_dtype="f32")
+    x = p.x.to(dev).view(T_HEAD, H_HEAD)
+    dy = p.dy.to(dev).view(T_HEAD, H_HEAD)
+    w = p.w.to(dev)
+    y, rstd = R.rmsnorm_train_fwd(x, w, p.eps)
+    plan_nd = R.rmsnorm_train_bwd_query(x, False)
+    plan_d = R.rmsnorm_train_bwd_query(x, True)
+    ws = torch.empty(max(plan_nd.workspace_bytes, plan_d.workspace_bytes), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+    return p, x, dy, w, rstd, ws, plan_nd, y
+
+
+def run_to_run(band, ev):
+    """Band of per-process medians: this process and the fresh ones."""
+    meds = [round(ev[len(ev) // 2] * 1e3, 2)] + [b["median_us"] for b in band]
+    lo, hi = min(meds), max(meds)
+    nbytes = bwd_bytes(T_HEAD, H_HEAD, 4)
+    return {"processes": len(meds), "median_us_per_process": meds, "band_us": [lo, hi],
+            "band_frac_of_peak": [round(nbytes / (hi * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                                  round(nbytes / (lo * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)],
+            "method": "median of the timed calls of each process (this one first, then fresh "
+                      "processes started before this one used the GPU); value and frac use this "
+                      "process's mean"}
+
+
+def band_child(args):
+    """One fresh process of the run-to-run band: the headline backward, K timed
+    calls after W warm-up calls; prints its per-call median and mean (us)."""
+    import torch
+
+    import rmsnorm_train_fwd_amd as R
+
+    p, x, dy, w, rstd, ws, _, y = headline_setup()
+    ev, _ = time_calls(lambda: R.rmsnorm_train_bwd(dy, x, rstd, w, False, workspace=ws),
+                       args.steps, args.warmup, torch)
+    print(json.dumps({"median_us": round(ev[len(ev) // 2] * 1e3, 2),
+                      "mean_us": round(sum(ev) / len(ev) * 1e3, 2)}), flush=True)
+
+
+def run_band(args):
+    """Per-process medians of the headline backward from args.band fresh
+    processes (the pages take the median of the calls of each process and
+    compare processes; where the caching allocator places x, dy and dx moves
+    this call by several percent on MI355X)."""
+    import subprocess
+
+    out = []
+    for i in range(args.band):
+        print(f"[bench] run-to-run band: process {i + 1} of {args.band}", file=sys.stderr,
+              flush=True)
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--band-child",
+                            "--steps", str(args.steps), "--warmup", str(args.warmup)],
+                           capture_output=True, text=True, timeout=600)
+        if r.returncode != 0:
+            raise SystemExit(f"bench.py: band process {i + 1} failed (exit {r.returncode}):\n"
+                             f"{r.stderr[-2000:]}")
+        out.append(json.loads(r.stdout.strip().splitlines()[-1]))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -723,6 +846,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=T_HEAD)
+    ap.add_argument("--band", type=int, default=2,
+                    help="fresh processes that repeat the headline timing for the run-to-run band")
+    ap.add_argument("--band-child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run the copy + backward calls that the counter runs read")
     ap.add_argument("--sweep", metavar="OUT.md",
@@ -762,24 +888,18 @@ def main():
         sweep(args.sweep)
         return
 
+    if args.band_child:
+        band_child(args)
+        return
+    # Fresh processes first, before this one touches the GPU: each times the
+    # same backward on its own allocation of the same inputs.
+    band = run_band(args) if args.band > 0 else []
+
     import torch
 
     import rmsnorm_train_fwd_amd as R
-    import synth
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    print(f"[bench] generating inputs [{T_HEAD}, {H_HEAD}]", file=sys.stderr, flush=True)
-    p = synth.make(T_HEAD, H_HEAD, seed=0, w_dtype="f32")
-    x = p.x.to(dev).view(T_HEAD, H_HEAD)
-    dy = p.dy.to(dev).view(T_HEAD, H_HEAD)
-    w = p.w.to(dev)
-    y, rstd = R.rmsnorm_train_fwd(x, w, p.eps)
-    plan_nd = R.rmsnorm_train_bwd_query(x, False)
-    plan_d = R.rmsnorm_train_bwd_query(x, True)
-    ws = torch.empty(max(plan_nd.workspace_bytes, plan_d.workspace_bytes), dtype=torch.uint8,
-                     device=dev)
-    torch.cuda.synchronize()
+    p, x, dy, w, rstd, ws, plan_nd, y = headline_setup()
 
     def bwd_nd():
         R.rmsnorm_train_bwd(dy, x, rstd, w, False, workspace=ws)
@@ -844,6 +964,7 @@ def main():
             "fwd_GBps": round(fwd_bytes(T_HEAD, H_HEAD, 4) / (med(ev_f) * 1e-3) / 1e9, 1),
             "ceiling": ceiling,
             "bwd_vs_r2w1_ceiling": round(gbps / ceiling["r2w1_GBps"], 4) if ceiling else None,
+            "run_to_run": run_to_run(band, ev),
             "baseline": {"us_per_call": PAGES_BWD_US_B200,
                          "GBps": round(nbytes / (PAGES_BWD_US_B200 * 1e-6) / 1e9, 1),
                          "hardware": "NVIDIA B200 (sm_100a)",

@@ -70,6 +70,11 @@ __device__ __forceinline__ uint4 ld16_stream(const u16* p) {
   u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+// Row outputs: 16-byte non-temporal stores. Write-through stores (system
+// scope, sc0 sc1) measured faster in single cold-cache calls, but only because
+// the memory-side cache then held up to its 256 MB of the call's output dirty
+// past the end of the call; back to back, where every byte reaches HBM, they
+// were equal or up to 5% slower at [131072, 4096].
 __device__ __forceinline__ void st16_stream(u16* p, const uint4& v) {
   u32x4_t t = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t*>(p));
