@@ -74,7 +74,7 @@ extern "C" {
 typedef enum {
   RMSN_OK = 0,
   RMSN_E_NULL = 1,        /* a required pointer is NULL */
-  RMSN_E_DTYPE = 2,       /* weight dtype code is not RMSN_BF16 / RMSN_F32 */
+  RMSN_E_DTYPE = 2,       /* unknown weight code, or a dw code other than RMSN_BF16 / RMSN_F32 */
   RMSN_E_SHAPE = 3,       /* T < 0, heads < 1, width unsupported, size overflow */
   RMSN_E_STRIDE = 4,      /* strides make rows overlap or run backwards */
   RMSN_E_ALIGN = 5,       /* misaligned pointer or stride */
@@ -85,7 +85,20 @@ typedef enum {
   RMSN_E_HIP = 10         /* the HIP runtime rejected a launch */
 } rmsn_status;
 
-typedef enum { RMSN_BF16 = 0, RMSN_F32 = 1 } rmsn_dtype;
+/* Storage format of w (and of dw, which takes RMSN_BF16 or RMSN_F32 only).
+ * The *_ZERO_CENTRED weight codes select the zero-centred-weight RMSNorm: the
+ * stored w is centred on zero and every formula below uses 1 + w in its place
+ * (rounded once to FP32 on the GPU); dw is then the gradient with respect to
+ * the stored w, which is the same sum. The pages name this variant only in
+ * the title of a related PR on the PR #8512 page ("zero-centred input
+ * RMSNorm") and never define it; this is the plainest reading that keeps the
+ * name RMSNorm (a mean-subtracted input would be LayerNorm). */
+typedef enum {
+  RMSN_BF16 = 0,
+  RMSN_F32 = 1,
+  RMSN_BF16_ZERO_CENTRED = 2,  /* w stored as BF16, used as 1 + w */
+  RMSN_F32_ZERO_CENTRED = 3    /* w stored as FP32, used as 1 + w */
+} rmsn_dtype;
 
 /* Row geometry (all counts and strides in elements). */
 typedef struct {

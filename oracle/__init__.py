@@ -52,6 +52,7 @@ def lib():
         L.orc_f64_to_bf16.argtypes = [C.c_double]
         L.orc_bf16_to_f64_array.argtypes = [u16p, C.c_int64, dp]
         L.orc_f64_to_bf16_array.argtypes = [dp, C.c_int64, u16p]
+        L.orc_zero_centred_weight.argtypes = [C.c_int64, dp, dp]
         L.orc_rmsnorm_fwd_f64.argtypes = [C.c_int64, C.c_int64, dp, dp, C.c_double, dp, dp]
         L.orc_rmsnorm_bwd_f64.argtypes = [C.c_int64, C.c_int64, dp, dp, dp, C.c_double, dp, dp]
         L.orc_gate_fwd_f64.argtypes = [C.c_int64, C.c_int64, dp, dp, dp, C.c_double, dp, dp]
@@ -94,6 +95,14 @@ def f64_to_bf16(a) -> np.ndarray:
     a = _f64(a)
     out = np.empty(a.shape, np.uint16)
     lib().orc_f64_to_bf16_array(_dp(a), a.size, out.ctypes.data_as(C.POINTER(C.c_uint16)))
+    return out
+
+
+def zero_centred_weight(w) -> np.ndarray:
+    """Effective weight 1 + w of the zero-centred form (float64)."""
+    w = _f64(w)
+    out = np.empty_like(w)
+    lib().orc_zero_centred_weight(w.size, _dp(w), _dp(out))
     return out
 
 

@@ -70,6 +70,13 @@ void orc_f64_to_bf16_array(const double* in, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = orc_f64_to_bf16(in[i]);
 }
 
+/* ---- zero-centred weight ------------------------------------------------ */
+
+void orc_zero_centred_weight(int64_t n, const double* w, double* out) {
+  /* The stored weight is centred on zero; the norm multiplies by 1 + w. */
+  for (int64_t j = 0; j < n; ++j) out[j] = 1.0 + w[j];
+}
+
 /* ---- one row ------------------------------------------------------------- */
 
 static double row_rstd(int64_t n, const double* x, double eps) {

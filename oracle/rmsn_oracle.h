@@ -23,6 +23,12 @@
  * The method's own formula is never printed on the pages. The oracle takes the
  * textbook RMSNorm: rstd = 1 / sqrt(sum_j x_j^2 / width + eps), eps inside the
  * root, mean over width, no (1 + w) offset, y_j = x_j * rstd * w_j.
+ *   - Zero-centred weight (PR #8512 page, the related-PR title "zero-centred
+ *     input RMSNorm", never defined there; read as the RMSNorm whose stored
+ *     weight is centred on zero and enters as 1 + w): every form above with
+ *     the effective weight 1 + w (orc_zero_centred_weight). The gradient with
+ *     respect to the stored w equals that with respect to 1 + w, so dw is the
+ *     same sum.
  *
  * Everything is computed in IEEE double from inputs converted exactly to double.
  * No blocking, fusion or reordering: rows in ascending order, columns in
@@ -54,6 +60,9 @@ double orc_bf16_to_f64(uint16_t b);        /* exact */
 uint16_t orc_f64_to_bf16(double d);        /* round to nearest, ties to even */
 void orc_bf16_to_f64_array(const uint16_t* in, int64_t n, double* out);
 void orc_f64_to_bf16_array(const double* in, int64_t n, uint16_t* out);
+
+/* Effective weight of the zero-centred form: out[j] = 1 + w[j] (in double). */
+void orc_zero_centred_weight(int64_t n, const double* w, double* out);
 
 /* ---- dense FP64 rows: x is [rows, width] row-major ------------------------ */
 void orc_rmsnorm_fwd_f64(int64_t rows, int64_t width, const double* x, const double* w,

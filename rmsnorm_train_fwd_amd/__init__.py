@@ -27,7 +27,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librmsnorm_train.so")
 
-RMSN_BF16, RMSN_F32 = 0, 1
+RMSN_BF16, RMSN_F32, RMSN_BF16_ZERO_CENTRED, RMSN_F32_ZERO_CENTRED = 0, 1, 2, 3
 PATH_AUTO, PATH_SMALL, PATH_LARGE = 0, 1, 2
 STATUS = {
     0: "RMSN_OK", 1: "RMSN_E_NULL", 2: "RMSN_E_DTYPE", 3: "RMSN_E_SHAPE", 4: "RMSN_E_STRIDE",
@@ -150,13 +150,14 @@ def _same_geometry(a: torch.Tensor, b: torch.Tensor, an: str, bn: str):
         raise ValueError(f"{bn} must have the shape and strides of {an}")
 
 
-def _w(w: torch.Tensor, width: int):
+def _w(w: torch.Tensor, width: int, zero_centred: bool = False):
+    """ABI weight code: storage dtype, plain or zero-centred (used as 1 + w)."""
     if w.dim() != 1 or w.shape[0] != width or not w.is_contiguous():
         raise ValueError(f"w must be a contiguous [{width}] vector")
     if w.dtype == torch.bfloat16:
-        return RMSN_BF16
+        return RMSN_BF16_ZERO_CENTRED if zero_centred else RMSN_BF16
     if w.dtype == torch.float32:
-        return RMSN_F32
+        return RMSN_F32_ZERO_CENTRED if zero_centred else RMSN_F32
     raise TypeError(f"w must be bfloat16 or float32, got {w.dtype}")
 
 
@@ -184,12 +185,13 @@ def _rows_shape(x: torch.Tensor):
 # -------------------------------------------------------------------- calls --
 
 def rmsnorm_train_fwd(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
-                      residual: Optional[torch.Tensor] = None):
+                      residual: Optional[torch.Tensor] = None, zero_centred: bool = False):
     """y = RMSNorm(x) * w (BF16) and rstd (FP32). With a residual: h = x + residual
-    (BF16) is normalised and returned as well: (y, rstd, h)."""
+    (BF16) is normalised and returned as well: (y, rstd, h). zero_centred: the
+    stored w is centred on zero and used as 1 + w."""
     _inner_contiguous(x, "x")
     L = _layout(x, None)
-    wd = _w(w, L.width)
+    wd = _w(w, L.width, zero_centred)
     if residual is not None:
         _same_geometry(x, residual, "x", "residual")
     _on_device(x, w=w, residual=residual)
@@ -236,13 +238,14 @@ def _dw(width: int, dtype: torch.dtype, device):
 def rmsnorm_train_bwd(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor, w: torch.Tensor,
                       deterministic: bool = True, dh: Optional[torch.Tensor] = None,
                       launch: Optional[Launch] = None, workspace: Optional[torch.Tensor] = None,
-                      dw_dtype: torch.dtype = torch.float32):
+                      dw_dtype: torch.dtype = torch.float32, zero_centred: bool = False):
     """dx (BF16) and dw (FP32, or BF16 with dw_dtype=torch.bfloat16). With dh
-    (residual form; x is then the forward's BF16 h): grad_h = dh + dx replaces dx."""
+    (residual form; x is then the forward's BF16 h): grad_h = dh + dx replaces dx.
+    zero_centred: w is used as 1 + w (dw is the gradient of the stored w)."""
     _inner_contiguous(x, "x")
     _inner_contiguous(dy, "dy")
     L = _layout(x, dy)
-    wd = _w(w, L.width)
+    wd = _w(w, L.width, zero_centred)
     if dh is not None:
         _same_geometry(dy, dh, "dy", "dh")
     _rstd(rstd, L)
@@ -262,12 +265,12 @@ def rmsnorm_train_bwd(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor, w: 
 
 
 def rmsnorm_silu_gate_train_fwd(x: torch.Tensor, z: torch.Tensor, w: torch.Tensor,
-                                eps: float = 1e-6):
-    """y = RMSNorm(x) * w * silu(z) (BF16) and rstd (FP32)."""
+                                eps: float = 1e-6, zero_centred: bool = False):
+    """y = RMSNorm(x) * w * silu(z) (BF16) and rstd (FP32); zero_centred: w used as 1 + w."""
     _inner_contiguous(x, "x")
     _same_geometry(x, z, "x", "z")
     L = _layout(x, None)
-    wd = _w(w, L.width)
+    wd = _w(w, L.width, zero_centred)
     _on_device(x, z=z, w=w)
     full, rows = _rows_shape(x)
     y = torch.empty(full, dtype=torch.bfloat16, device=x.device)
@@ -283,14 +286,15 @@ def rmsnorm_silu_gate_train_bwd(dy: torch.Tensor, x: torch.Tensor, z: torch.Tens
                                 rstd: torch.Tensor, w: torch.Tensor, deterministic: bool = True,
                                 launch: Optional[Launch] = None,
                                 workspace: Optional[torch.Tensor] = None,
-                                dw_dtype: torch.dtype = torch.float32):
+                                dw_dtype: torch.dtype = torch.float32,
+                                zero_centred: bool = False):
     """dx, dz (BF16) and dw (FP32, or BF16 with dw_dtype=torch.bfloat16) of the
-    SiLU-gated form."""
+    SiLU-gated form; zero_centred: w used as 1 + w."""
     _inner_contiguous(x, "x")
     _inner_contiguous(dy, "dy")
     _same_geometry(x, z, "x", "z")
     L = _layout(x, dy)
-    wd = _w(w, L.width)
+    wd = _w(w, L.width, zero_centred)
     _rstd(rstd, L)
     _on_device(x, dy=dy, z=z, rstd=rstd, w=w, workspace=workspace)
     plan = rmsnorm_train_bwd_query(x, deterministic, launch, dy)
@@ -312,7 +316,7 @@ def rmsnorm_silu_gate_train_bwd(dy: torch.Tensor, x: torch.Tensor, z: torch.Tens
 def rmsnorm_train_bwd_noalloc(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor,
                               w: torch.Tensor, deterministic: bool = True,
                               dh: Optional[torch.Tensor] = None, launch: Optional[Launch] = None,
-                              dw_dtype: torch.dtype = torch.float32):
+                              dw_dtype: torch.dtype = torch.float32, zero_centred: bool = False):
     """rmsnorm_train_bwd through the library's workspace-free entry point (its
     workspace is a device array inside the library, shared by every call on a
     GPU: calls that can overlap in time on one GPU race). Same results, bit for
@@ -320,7 +324,7 @@ def rmsnorm_train_bwd_noalloc(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Ten
     _inner_contiguous(x, "x")
     _inner_contiguous(dy, "dy")
     L = _layout(x, dy)
-    wd = _w(w, L.width)
+    wd = _w(w, L.width, zero_centred)
     if dh is not None:
         _same_geometry(dy, dh, "dy", "dh")
     _rstd(rstd, L)

@@ -114,6 +114,16 @@ rmsn_status check_launch(const rmsn_launch* o) {
 
 bool eps_ok(float eps) { return isfinite(eps) && eps >= 0.0f; }
 
+// Weight codes: BF16 or FP32 storage, plain or zero-centred (1 + w).
+bool w_code_ok(int c) {
+  return c == RMSN_BF16 || c == RMSN_F32 || c == RMSN_BF16_ZERO_CENTRED ||
+         c == RMSN_F32_ZERO_CENTRED;
+}
+bool w_is_f32(int c) { return c == RMSN_F32 || c == RMSN_F32_ZERO_CENTRED; }
+int w_zero_centred(int c) {
+  return c == RMSN_BF16_ZERO_CENTRED || c == RMSN_F32_ZERO_CENTRED ? 1 : 0;
+}
+
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 void make_plan(const rmsn_layout& L, int /*det*/, const rmsn_launch* o, rmsn_bwd_plan* p) {
@@ -172,7 +182,7 @@ rmsn_status bwd_common(int form, const void* dy, const void* x, const void* e, c
                        void* stream) {
   rmsn_status st = check_layout(L);
   if (st) return st;
-  if (w_dtype != RMSN_BF16 && w_dtype != RMSN_F32) return RMSN_E_DTYPE;
+  if (!w_code_ok(w_dtype)) return RMSN_E_DTYPE;
   if (dw_dtype != RMSN_BF16 && dw_dtype != RMSN_F32) return RMSN_E_DTYPE;
   if (det != 0 && det != 1) return RMSN_E_ARG;
   if ((st = check_launch(o))) return st;
@@ -197,7 +207,7 @@ rmsn_status bwd_common(int form, const void* dy, const void* x, const void* e, c
     if (!aligned(ws, 16)) return RMSN_E_ALIGN;
   }
   const int64_t W = L->width;
-  const int64_t wbytes = W * (w_dtype == RMSN_F32 ? 4 : 2);
+  const int64_t wbytes = W * (w_is_f32(w_dtype) ? 4 : 2);
   const int64_t rbytes = rows * W * 2;
   const bool e_uses_g = (form == kResidual);
   const Span ins[] = {
@@ -235,7 +245,8 @@ rmsn_status bwd_common(int form, const void* dy, const void* x, const void* e, c
   a.rows = rows;
   a.chunks = plan.chunks;
   a.heads = (int32_t)L->heads;
-  const bool wf32 = (w_dtype == RMSN_F32);
+  a.w_one = w_zero_centred(w_dtype);
+  const bool wf32 = w_is_f32(w_dtype);
   const hipStream_t s = as_stream(stream);
   hipError_t err;
   if (plan.path == RMSN_PATH_SMALL) {
@@ -286,7 +297,7 @@ static rmsn_status fwd_common(int form, const void* x, const void* e, const void
                               void* h_out, float* rstd, void* stream) {
   rmsn_status st = check_layout(L);
   if (st) return st;
-  if (w_dtype != RMSN_BF16 && w_dtype != RMSN_F32) return RMSN_E_DTYPE;
+  if (!w_code_ok(w_dtype)) return RMSN_E_DTYPE;
   if (!eps_ok(eps)) return RMSN_E_ARG;
   const int64_t rows = L->T * L->heads;
   if (!w) return RMSN_E_NULL;
@@ -304,7 +315,7 @@ static rmsn_status fwd_common(int form, const void* x, const void* e, const void
   const Span ins[] = {
       row_span(x, *L, L->x_stride_t, L->x_stride_h),
       row_span(e, *L, L->x_stride_t, L->x_stride_h),
-      dense_span(w, W * (w_dtype == RMSN_F32 ? 4 : 2)),
+      dense_span(w, W * (w_is_f32(w_dtype) ? 4 : 2)),
   };
   const Span outs[] = {dense_span(y, rbytes), dense_span(h_out, rbytes), dense_span(rstd, rows * 4)};
   for (const Span& a : outs) {
@@ -324,10 +335,11 @@ static rmsn_status fwd_common(int form, const void* x, const void* e, const void
   a.rstd = rstd;
   a.rows = rows;
   a.heads = (int32_t)L->heads;
+  a.w_one = w_zero_centred(w_dtype);
   a.eps = eps;
   const int64_t tiles = cdiv(rows, fwd_rows_per_tile((int)W, form));
   const int grid = (int)(tiles < kMaxGrid ? tiles : kMaxGrid);
-  hipError_t err = launch_fwd((int)W, w_dtype == RMSN_F32, form, a, grid, as_stream(stream));
+  hipError_t err = launch_fwd((int)W, w_is_f32(w_dtype), form, a, grid, as_stream(stream));
   return err == hipSuccess ? RMSN_OK : RMSN_E_HIP;
 }
 

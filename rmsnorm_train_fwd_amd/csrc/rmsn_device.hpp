@@ -197,9 +197,10 @@ __device__ __forceinline__ int elem0(int v, int lane) {
   return (v * G::TPR + lane) * 8;
 }
 
-// Weight in registers: the E elements a thread owns, as FP32.
+// Weight in registers: the E elements a thread owns, as FP32. With `one`
+// set (zero-centred weight) each becomes 1 + w, rounded once to FP32.
 template <class G, bool WF32>
-__device__ __forceinline__ void load_w(const void* w, int lane, float (&wr)[G::E]) {
+__device__ __forceinline__ void load_w(const void* w, int lane, float (&wr)[G::E], int one) {
   constexpr int TPR = G::TPR;
 #pragma unroll
   for (int v = 0; v < G::V; ++v) {
@@ -215,6 +216,10 @@ __device__ __forceinline__ void load_w(const void* w, int lane, float (&wr)[G::E
 #pragma unroll
       for (int i = 0; i < 8; ++i) wr[v * 8 + i] = f[i];
     }
+  }
+  if (one) {
+#pragma unroll
+    for (int i = 0; i < G::E; ++i) wr[i] = 1.0f + wr[i];
   }
 }
 

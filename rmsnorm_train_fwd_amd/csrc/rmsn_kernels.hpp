@@ -93,7 +93,7 @@ __global__ __launch_bounds__((FGeo<H, FORM>::BLOCK)) void k_fwd(FwdArgs a) {
   __shared__ float slots[RowSum<G, RPG>::kSlots];
   int parity = 0;
   float wr[E];
-  load_w<G, WF32>(a.w, lane, wr);
+  load_w<G, WF32>(a.w, lane, wr, a.w_one);
 
   const int64_t tiles = (a.rows + R * RPG - 1) / (R * RPG);
   for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(Geo<H>::BLOCK) void k_bwd_large(BwdArgs a) {
   __shared__ double merge[R >= 4 ? R * H : (R > 1 ? H : 1)];
   int parity = 0;
   float wr[E];
-  load_w<G, WF32>(a.w, lane, wr);
+  load_w<G, WF32>(a.w, lane, wr, a.w_one);
   const int64_t K = a.chunks, tiles = (a.rows + R - 1) / R;
 
   for (int64_t k = blockIdx.x; k < K; k += gridDim.x) {
@@ -547,7 +547,7 @@ __global__ __launch_bounds__(SmallGeo<H>::BLOCK) void k_bwd_small(BwdArgs a, int
     const int q = row_group<G>(), lane = threadIdx.x % TPR;
     int parity = 0;
     float wr[G::E];
-    load_w<G, WF32>(a.w, lane, wr);
+    load_w<G, WF32>(a.w, lane, wr, a.w_one);
     const int64_t tiles = (a.rows + RS - 1) / RS;
     for (int64_t t = blockIdx.x - col_grid; t < tiles; t += row_grid) {
       bool ok[1] = {t * RS + q < a.rows};

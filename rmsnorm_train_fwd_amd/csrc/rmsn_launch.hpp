@@ -24,6 +24,7 @@ struct FwdArgs {
   float* rstd;        // [rows]
   int64_t rows;
   int32_t heads;
+  int32_t w_one;      // 1: zero-centred weight, the kernels use 1 + w
   float eps;
 };
 
@@ -41,6 +42,7 @@ struct BwdArgs {
   int64_t rows;
   int64_t chunks;     // K: chunks of the dw tree, 1 <= K <= ceil(rows / R) when rows > 0
   int32_t heads;
+  int32_t w_one;      // 1: zero-centred weight, the kernels use 1 + w
 };
 
 // Each returns the status of its own launches (hipLaunchKernel's result;

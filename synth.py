@@ -44,9 +44,10 @@ def normal_bf16(shape, seed: int, salt: int, scale: float = 1.0) -> torch.Tensor
     return t.to(torch.bfloat16)
 
 
-def weight(width: int, seed: int, w_dtype: str = "f32") -> torch.Tensor:
-    """w = 1 + 0.1 N(0,1), FP32, or cast once to BF16."""
-    w = torch.randn(width, generator=_gen(seed, 7), dtype=torch.float32).mul_(0.1).add_(1.0)
+def weight(width: int, seed: int, w_dtype: str = "f32", centre: float = 1.0) -> torch.Tensor:
+    """w = centre + 0.1 N(0,1), FP32, or cast once to BF16 (centre 1 for the
+    plain weight, 0 for a zero-centred one)."""
+    w = torch.randn(width, generator=_gen(seed, 7), dtype=torch.float32).mul_(0.1).add_(centre)
     if w_dtype == "bf16":
         return w.to(torch.bfloat16)
     if w_dtype == "f32":
@@ -123,8 +124,9 @@ class Problem:
 
 def make(T: int, width: int, seed: int = 0, heads: int = 1, w_dtype: str = "f32",
          family: str = "normal", form: str = "plain", row_stride: Optional[int] = None,
-         head_stride: Optional[int] = None) -> Problem:
-    """form: 'plain', 'residual' (extra = residual, dh given) or 'gate' (extra = z)."""
+         head_stride: Optional[int] = None, w_centre: float = 1.0) -> Problem:
+    """form: 'plain', 'residual' (extra = residual, dh given) or 'gate' (extra = z).
+    w_centre: the weight's centre (1, or 0 for the zero-centred-weight form)."""
     hs = width if head_stride is None else head_stride
     rs = heads * hs if row_stride is None else row_stride
     x = row_buffer(T, heads, width, seed, 1, family, rs, hs, role="x")
@@ -137,4 +139,5 @@ def make(T: int, width: int, seed: int = 0, heads: int = 1, w_dtype: str = "f32"
         extra = row_buffer(T, heads, width, seed, 5, "normal", rs, hs, role="z")
     elif form != "plain":
         raise ValueError(form)
-    return Problem(T, heads, width, rs, hs, weight(width, seed, w_dtype), x, dy, extra, dh)
+    return Problem(T, heads, width, rs, hs, weight(width, seed, w_dtype, w_centre), x, dy, extra,
+                   dh)

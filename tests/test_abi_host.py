@@ -93,6 +93,10 @@ def test_fwd_validation_errors():
     assert fwd(L, a["x"], a["res"], a["w"], a["y"], None, a["rstd"]) == E_NULL  # residual w/o h_out
     assert fwd(L, a["x"], None, a["w"], a["y"], a["h"], a["rstd"]) == E_ARG     # h_out w/o residual
     assert fwd(L, a["x"], None, a["w"], a["y"], None, a["rstd"], wd=7) == E_DTYPE
+    assert fwd(L, a["x"], None, a["w"], a["y"], None, a["rstd"], wd=4) == E_DTYPE
+    if not gpu_visible():  # both zero-centred codes pass validation
+        for wd in (R.RMSN_BF16_ZERO_CENTRED, R.RMSN_F32_ZERO_CENTRED):
+            assert fwd(L, a["x"], None, a["w"], a["y"], None, a["rstd"], wd=wd) == E_HIP
     for eps in (float("nan"), float("inf"), -1e-6):
         assert fwd(L, a["x"], None, a["w"], a["y"], None, a["rstd"], eps=eps) == E_ARG
     for W in (0, 128, 1000, 4097, 8192):
@@ -151,7 +155,17 @@ def test_bwd_validation_errors():
         assert bwd(**args(**{k: None})) == E_NULL, k
     assert bwd(**args(det=2)) == E_ARG
     assert bwd(**args(wd=5)) == E_DTYPE
+    assert bwd(**args(wd=4)) == E_DTYPE
+    assert bwd(**args(wd=-1)) == E_DTYPE
     assert bwd(**args(dwd=2)) == E_DTYPE               # dw is FP32 or BF16
+    assert bwd(**args(dwd=R.RMSN_F32_ZERO_CENTRED)) == E_DTYPE
+    # the zero-centred weight codes keep their storage size: a dw right after a
+    # BF16 w's 512 elements touches a FP32 w's extent only
+    W = 512
+    assert bwd(**args(dw=a["w"] + 2 * W, wd=R.RMSN_F32_ZERO_CENTRED)) == E_ALIAS
+    if not gpu_visible():
+        assert bwd(**args(dw=a["w"] + 2 * W, wd=R.RMSN_BF16_ZERO_CENTRED)) == E_HIP
+        assert bwd(**args(wd=R.RMSN_F32_ZERO_CENTRED)) == E_HIP
     # the dw extent follows its dtype: 512 FP32 values starting 1 KiB below rstd
     # reach into rstd, 512 BF16 values end exactly at it
     assert bwd(**args(dw=a["rstd"] - 1024)) == E_ALIAS

@@ -24,31 +24,37 @@ WIDTHS = (512, 1536, 2048, 4096, 5120, 6144)
 SMALL_T = (1, 2, 4, 8, 16, 32, 64, 128, 203)
 
 
-def run_case(p: synth.Problem, det=True, form="plain", launch=None, nsample=None, seed=0):
+def run_case(p: synth.Problem, det=True, form="plain", launch=None, nsample=None, seed=0,
+             zero_centred=False):
     """fwd + bwd on the GPU, checked against the oracle. `det` is one mode or a
     tuple of modes: the forward and the oracle run once and every mode's
-    backward is checked against them. Returns error ratios (of the last mode)."""
+    backward is checked against them. zero_centred: the stored w is used as
+    1 + w (the oracle gets that effective weight). Returns error ratios (of the
+    last mode)."""
     modes = tuple(det) if isinstance(det, (tuple, list)) else (det,)
+    zc = dict(zero_centred=zero_centred)
     g = OnGpu(p)
     bwd_out = {}
     if form == "residual":
-        y, rstd, h = R.rmsnorm_train_fwd(g.x, g.w, p.eps, residual=g.e)
+        y, rstd, h = R.rmsnorm_train_fwd(g.x, g.w, p.eps, residual=g.e, **zc)
         for m in modes:
-            bwd_out[m] = R.rmsnorm_train_bwd(g.dy, h, rstd, g.w, m, dh=g.dh, launch=launch) + (None,)
+            bwd_out[m] = R.rmsnorm_train_bwd(g.dy, h, rstd, g.w, m, dh=g.dh, launch=launch,
+                                             **zc) + (None,)
     elif form == "gate":
-        y, rstd = R.rmsnorm_silu_gate_train_fwd(g.x, g.e, g.w, p.eps)
+        y, rstd = R.rmsnorm_silu_gate_train_fwd(g.x, g.e, g.w, p.eps, **zc)
         for m in modes:
-            dx, dz, dw = R.rmsnorm_silu_gate_train_bwd(g.dy, g.x, g.e, rstd, g.w, m, launch=launch)
+            dx, dz, dw = R.rmsnorm_silu_gate_train_bwd(g.dy, g.x, g.e, rstd, g.w, m, launch=launch,
+                                                       **zc)
             bwd_out[m] = (dx, dw, dz)
     else:
-        y, rstd = R.rmsnorm_train_fwd(g.x, g.w, p.eps)
+        y, rstd = R.rmsnorm_train_fwd(g.x, g.w, p.eps, **zc)
         for m in modes:
-            bwd_out[m] = R.rmsnorm_train_bwd(g.dy, g.x, rstd, g.w, m, launch=launch) + (None,)
+            bwd_out[m] = R.rmsnorm_train_bwd(g.dy, g.x, rstd, g.w, m, launch=launch, **zc) + (None,)
     torch.cuda.synchronize()
 
     rows, W = p.rows, p.width
     sel = sample_rows(rows, nsample, seed) if nsample else np.arange(rows, dtype=np.int64)
-    w64 = w_f64(p.w)
+    w64 = oracle.zero_centred_weight(w_f64(p.w)) if zero_centred else w_f64(p.w)
     xo, dyo = oview(p, p.x), oview(p, p.dy)
     out = {}
     if form == "residual":

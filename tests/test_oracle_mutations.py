@@ -37,6 +37,8 @@ MUTATIONS = {
     "gate_bwd_view_z_from_x": ("if (z) load_row(z, r, zr);", "if (z) load_row(x, r, zr);"),
     "gate_bwd_view_dw_z_from_x": ("if (z) load_row(z, r, zr);\n      row_bwd(n, gr, xr, z ? zr : NULL, w, eps, NULL, NULL, dw);",
                                   "if (z) load_row(x, r, zr);\n      row_bwd(n, gr, xr, z ? zr : NULL, w, eps, NULL, NULL, dw);"),
+    "zero_centred_offset_missing": ("out[j] = 1.0 + w[j];", "out[j] = w[j];"),
+    "zero_centred_offset_doubled": ("out[j] = 1.0 + w[j];", "out[j] = 2.0 + w[j];"),
     "gate_fwd_sel_ignored": ("int64_t r = sel ? sel[i] : i;\n    load_row(x, r, xr);\n    load_row(z, r, zr);",
                              "int64_t r = i;\n    load_row(x, r, xr);\n    load_row(z, r, zr);"),
 }

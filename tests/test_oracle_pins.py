@@ -474,3 +474,52 @@ def test_gate_view_entry_points_equal_dense_cores_with_separate_z():
     # the inputs discriminate: with z read through x's view the results move
     y_xz, _ = oracle.gate_fwd_f64(xd, xd, w, EPS)
     assert not np.allclose(y_xz, y)
+
+
+# --------------------------------------------------- zero-centred weight ---
+# The related-PR title "zero-centred input RMSNorm" on the PR #8512 page, read
+# as the RMSNorm whose stored weight is centred on zero and enters as 1 + w.
+
+def test_zero_centred_weight_zero_is_the_unit_gain_norm():
+    rng = np.random.default_rng(16)
+    x = rng.standard_normal((4, 48))
+    dy = rng.standard_normal((4, 48))
+    w_eff = oracle.zero_centred_weight(np.zeros(48))
+    assert np.array_equal(w_eff, np.ones(48))
+    y, r = oracle.rmsnorm_fwd_f64(x, w_eff, EPS)
+    # closed form: y = x / sqrt(mean x^2 + eps)
+    ref = x / np.sqrt((x * x).mean(axis=1, keepdims=True) + EPS)
+    assert np.allclose(y, ref, rtol=1e-15, atol=0)
+    # and the stored value enters once, as 1 + w
+    w = rng.standard_normal(48) * 0.1
+    assert np.array_equal(oracle.zero_centred_weight(w), 1.0 + w)
+
+
+def test_zero_centred_weight_matches_complex_step_of_its_own_loss():
+    # loss = sum dy * xhat * (1 + w), written here over complex numbers; its
+    # derivatives w.r.t. x and the stored w are the oracle's dx and dw taken
+    # with the effective weight 1 + w (plain and gated forms)
+    rng = np.random.default_rng(17)
+    rows, n = 3, 10
+    x = rng.standard_normal((rows, n))
+    z = rng.standard_normal((rows, n))
+    dy = rng.standard_normal((rows, n))
+    w = 0.1 * rng.standard_normal(n)
+
+    def fwd_zc(xc, wc, zc=None):
+        r = 1.0 / np.sqrt((xc * xc).sum(axis=-1, keepdims=True) / n + EPS)
+        y = xc * r * (1.0 + wc)
+        return y if zc is None else y * (zc / (1.0 + np.exp(-zc)))
+
+    dx, dw = oracle.rmsnorm_bwd_f64(dy, x, oracle.zero_centred_weight(w), EPS)
+    gx = _complex_step_grad(lambda c: (dy * fwd_zc(c, w)).sum(), x)
+    gw = _complex_step_grad(lambda c: (dy * fwd_zc(x, c)).sum(), w)
+    assert np.allclose(dx, gx, rtol=1e-12, atol=1e-14)
+    assert np.allclose(dw, gw, rtol=1e-12, atol=1e-14)
+    dxg, dzg, dwg = oracle.gate_bwd_f64(dy, x, z, oracle.zero_centred_weight(w), EPS)
+    assert np.allclose(dxg, _complex_step_grad(lambda c: (dy * fwd_zc(c, w, z)).sum(), x),
+                       rtol=1e-12, atol=1e-14)
+    assert np.allclose(dzg, _complex_step_grad(lambda c: (dy * fwd_zc(x, w, c)).sum(), z),
+                       rtol=1e-12, atol=1e-14)
+    assert np.allclose(dwg, _complex_step_grad(lambda c: (dy * fwd_zc(x, c, z)).sum(), w),
+                       rtol=1e-12, atol=1e-14)
