@@ -28,7 +28,8 @@ T_HEAD, H_HEAD = 131072, 4096
 # with FP32 weight ("new us" column). Context for vs_baseline, not a target.
 PAGES_BWD_US_B200 = 489.86
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_131072x4096.json")
-KERNEL_SOURCES = ["rmsn_kernels.hpp", "rmsn_device.hpp", "rmsn_bwd_large.hip", "rmsn_launch.hpp", "rmsn_abi.cpp"]
+KERNEL_SOURCES = ["rmsn_kernels.hpp", "rmsn_device.hpp", "rmsn_bwd_large.hip", "rmsn_fwd.hip",
+                  "rmsn_launch.hpp", "rmsn_abi.cpp"]
 
 
 def bwd_bytes(T, H, w_bytes):
@@ -653,7 +654,7 @@ def stats_report(stats_csv, out_md, command):
                      f"{float(r['MaxNs']) / 1e3:.1f} | {gb} |")
     lines += ["", "k_bwd_large template arguments: <width, FP32 weight, form (0 = plain), "
               "deterministic, rows per batch>. One backward call = k_bwd_large + k_fold.",
-              "k_stream / k_stream_oneshot: the bandwidth probe (librmsn_probe.so) over the same "
+              "k_stream / k_stream_oneshot: the bandwidth probe (probe/librmsn_probe.so) over the same "
               "tensors, no arithmetic: the dealt-tile pattern of the kernels and a one-shot "
               "pattern; <nin> = tensors read (0 = read only, nothing written)."]
     with open(out_md, "w") as fh:
@@ -892,8 +893,14 @@ def main():
         band_child(args)
         return
     # Fresh processes first, before this one touches the GPU: each times the
-    # same backward on its own allocation of the same inputs.
-    band = run_band(args) if args.band > 0 else []
+    # same backward on its own allocation of the same inputs. Under a profiler
+    # (its library preloaded) the GPU is initialised before this program
+    # starts, so no child process is started from it and the band is skipped.
+    profiled = "rocprof" in os.environ.get("LD_PRELOAD", "")
+    if profiled and args.band > 0:
+        print("[bench] run-to-run band skipped: running under a profiler", file=sys.stderr,
+              flush=True)
+    band = run_band(args) if args.band > 0 and not profiled else []
 
     import torch
 
