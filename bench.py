@@ -102,10 +102,10 @@ def stream_ceiling(x, dy, steps, torch):
     assert dy.numel() * dy.element_size() == nbytes and x.is_contiguous() and dy.is_contiguous()
     out = torch.empty_like(x)
     stream = torch.cuda.current_stream().cuda_stream
-    out_ = {"by_pattern": {"dealt": {}, "oneshot": {}}}
+    out_ = {"by_pattern": {"dealt": {}, "oneshot": {}, "oneshot_vec1": {}}}
     for nin, key, moved in ((2, "r2w1_GBps", 3 * nbytes), (1, "r1w1_GBps", 2 * nbytes),
                             (0, "r1_GBps", nbytes)):
-        for pattern, name in ((0, "dealt"), (1, "oneshot")):
+        for pattern, name in ((0, "dealt"), (1, "oneshot"), (2, "oneshot_vec1")):
             def call():
                 rc = f(nin, pattern, x.data_ptr(), dy.data_ptr(), out.data_ptr(), nbytes, 256,
                        stream)
@@ -114,10 +114,12 @@ def stream_ceiling(x, dy, steps, torch):
             ev, _ = time_calls(call, steps, 3, torch)
             out_["by_pattern"][name][key] = round(moved / (sum(ev) / len(ev) * 1e-3) / 1e9, 1)
         out_[key] = max(v[key] for v in out_["by_pattern"].values())
-    out_["probe"] = ("the backward's x and dy in 16 KiB tiles, 16-byte non-temporal accesses, no "
-                     "arithmetic; dealt: 256 workgroups x 1024 threads, tiles dealt in turn, next "
+    out_["probe"] = ("the backward's x and dy, 16-byte non-temporal accesses, no arithmetic; "
+                     "dealt: 256 workgroups x 1024 threads, 16 KiB tiles dealt in turn, next "
                      "tile's loads in flight (the kernels' pattern); oneshot: one 256-thread "
-                     "workgroup per tile; the ceiling is the faster of the two")
+                     "workgroup per 16 KiB tile, 4 vectors per thread; oneshot_vec1: one "
+                     "256-thread workgroup per 4 KiB, one vector per thread; the ceiling is the "
+                     "fastest of the three")
     return out_
 
 
@@ -654,9 +656,10 @@ def stats_report(stats_csv, out_md, command):
                      f"{float(r['MaxNs']) / 1e3:.1f} | {gb} |")
     lines += ["", "k_bwd_large template arguments: <width, FP32 weight, form (0 = plain), "
               "deterministic, rows per batch>. One backward call = k_bwd_large + k_fold.",
-              "k_stream / k_stream_oneshot: the bandwidth probe (probe/librmsn_probe.so) over the same "
-              "tensors, no arithmetic: the dealt-tile pattern of the kernels and a one-shot "
-              "pattern; <nin> = tensors read (0 = read only, nothing written)."]
+              "k_stream / k_stream_oneshot / k_stream_vec1: the bandwidth probe "
+              "(probe/librmsn_probe.so) over the same tensors, no arithmetic: the dealt-tile "
+              "pattern of the kernels, a one-shot pattern with 4 vectors per thread and one with "
+              "one vector per thread; <nin> = tensors read (0 = read only, nothing written)."]
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))

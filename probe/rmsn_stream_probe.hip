@@ -12,8 +12,11 @@
 //     backward's chunks do; one vector per thread per tile, and the loads of a
 //     workgroup's next tile are in flight while the current one is written.
 //   pattern 1 (one-shot): one 256-thread workgroup per tile, four vectors per
-//     thread, consecutive workgroups on consecutive tiles (the plainest
-//     streaming kernel; `grid` is ignored).
+//     thread, consecutive workgroups on consecutive tiles (`grid` is ignored).
+//   pattern 2 (one-shot, one vector): one 256-thread workgroup per 4 KiB, one
+//     vector per thread (the plainest streaming kernel, and the fastest of a
+//     sweep of block sizes, vectors per thread and grid-strided forms on
+//     MI355X; `grid` is ignored).
 //   nin = 1: out = a           (one stream read, one written: the forward)
 //   nin = 2: out = a ^ b       (two read, one written: the backward)
 //   nin = 0: a is read and folded into one vector per thread (read only)
@@ -84,18 +87,40 @@ __global__ __launch_bounds__(256) void k_stream_oneshot(const v4u* __restrict__ 
   if constexpr (NIN == 0) out[base] = acc;
 }
 
+template <int NIN>
+__global__ __launch_bounds__(256) void k_stream_vec1(const v4u* __restrict__ a,
+                                                      const v4u* __restrict__ b,
+                                                      v4u* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  v4u va = __builtin_nontemporal_load(a + i);
+  if constexpr (NIN == 0) {
+    // read only: a store the data practically never asks for keeps the load live
+    if ((va.x ^ va.y ^ va.z ^ va.w) == 0x9e3779b9u) out[blockIdx.x] = va;
+  } else {
+    if constexpr (NIN == 2) va ^= __builtin_nontemporal_load(b + i);
+    __builtin_nontemporal_store(va, out + i);
+  }
+}
+
+// Enqueues k<<<grid, block, 0, s>>>(args) and returns that launch's own status.
+template <class... P>
+int launch(void (*k)(P...), unsigned grid, unsigned block, hipStream_t s, P... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(k), dim3(grid), dim3(block), argv, 0, s);
+}
+
 }  // namespace
 
 // Runs one probe pass over `bytes` bytes per stream, a multiple of 16 KiB, in
-// pattern 0 or 1 as above. nin is 0, 1 or 2 as above; b is read only for
+// pattern 0, 1 or 2 as above. nin is 0, 1 or 2 as above; b is read only for
 // nin = 2; with nin = 0, out receives at most `bytes`. Returns a hipError_t
 // value: hipErrorInvalidValue for bad arguments, before any launch.
 extern "C" __attribute__((visibility("default"))) int rmsn_stream_probe(
     int nin, int pattern, const void* a, const void* b, void* out, int64_t bytes, int grid,
     void* stream) {
-  if (nin < 0 || nin > 2 || pattern < 0 || pattern > 1 || a == nullptr || out == nullptr ||
+  if (nin < 0 || nin > 2 || pattern < 0 || pattern > 2 || a == nullptr || out == nullptr ||
       (nin == 2 && b == nullptr) || bytes <= 0 || bytes % kTileBytes != 0 ||
-      bytes / kTileBytes > 0x7fffffff || grid < 1 || grid > 65535 ||
+      bytes / kTileBytes > 0x1fffffff || grid < 1 || grid > 65535 ||
       ((uintptr_t)a | (uintptr_t)b | (uintptr_t)out) % 16 != 0)
     return (int)hipErrorInvalidValue;
   const int64_t tiles = bytes / kTileBytes;
@@ -106,16 +131,22 @@ extern "C" __attribute__((visibility("default"))) int rmsn_stream_probe(
   if (pattern == 1) {
     const unsigned g = (unsigned)tiles;
     switch (nin) {
-      case 0: k_stream_oneshot<0><<<g, 256, 0, s>>>(pa, pb, po); break;
-      case 1: k_stream_oneshot<1><<<g, 256, 0, s>>>(pa, pb, po); break;
-      default: k_stream_oneshot<2><<<g, 256, 0, s>>>(pa, pb, po); break;
+      case 0: return launch(k_stream_oneshot<0>, g, 256, s, pa, pb, po);
+      case 1: return launch(k_stream_oneshot<1>, g, 256, s, pa, pb, po);
+      default: return launch(k_stream_oneshot<2>, g, 256, s, pa, pb, po);
     }
-    return (int)hipGetLastError();
+  }
+  if (pattern == 2) {
+    const unsigned g = (unsigned)(tiles * 4);  // 4 KiB per workgroup
+    switch (nin) {
+      case 0: return launch(k_stream_vec1<0>, g, 256, s, pa, pb, po);
+      case 1: return launch(k_stream_vec1<1>, g, 256, s, pa, pb, po);
+      default: return launch(k_stream_vec1<2>, g, 256, s, pa, pb, po);
+    }
   }
   switch (nin) {
-    case 0: k_stream<0><<<grid, kBlock, 0, s>>>(pa, pb, po, tiles); break;
-    case 1: k_stream<1><<<grid, kBlock, 0, s>>>(pa, pb, po, tiles); break;
-    default: k_stream<2><<<grid, kBlock, 0, s>>>(pa, pb, po, tiles); break;
+    case 0: return launch(k_stream<0>, (unsigned)grid, (unsigned)kBlock, s, pa, pb, po, tiles);
+    case 1: return launch(k_stream<1>, (unsigned)grid, (unsigned)kBlock, s, pa, pb, po, tiles);
+    default: return launch(k_stream<2>, (unsigned)grid, (unsigned)kBlock, s, pa, pb, po, tiles);
   }
-  return (int)hipGetLastError();
 }

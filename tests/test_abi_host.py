@@ -262,7 +262,7 @@ def test_bandwidth_probe_library_loads_and_rejects_bad_arguments():
     a, b, o = 1 << 20, 2 << 20, 3 << 20  # 16-byte aligned stand-ins, never dereferenced
     tile = 16 << 10
     assert f(3, 0, a, b, o, tile, 256, None) == invalid       # nin out of range
-    assert f(2, 2, a, b, o, tile, 256, None) == invalid       # pattern out of range
+    assert f(2, 3, a, b, o, tile, 256, None) == invalid       # pattern out of range
     assert f(2, 0, a, None, o, tile, 256, None) == invalid    # two inputs need b
     assert f(1, 0, a, None, None, tile, 256, None) == invalid  # no output
     assert f(1, 0, a, None, o, tile + 16, 256, None) == invalid  # not whole 16 KiB tiles
