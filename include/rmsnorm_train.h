@@ -40,9 +40,11 @@
  * Conventions for every call:
  *  - Pointers are DEVICE pointers unless stated. The caller owns every buffer,
  *    including the workspace. The library never allocates, frees or
- *    synchronises, keeps no pointer after return and has no mutable global
- *    state; calls are asynchronous on `stream` (a hipStream_t; NULL = the
- *    default stream).
+ *    synchronises and keeps no pointer after return; calls are asynchronous
+ *    on `stream` (a hipStream_t; NULL = the default stream). Its only mutable
+ *    global state is the per-device address of the device array behind
+ *    rmsnorm_train_bwd_noalloc, looked up once per device under a lock; every
+ *    other call is free of shared state and safe from several host threads.
  *  - Rows: a layout describes T tokens x `heads` rows per token; row
  *    r = t*heads + h of a row input starts at base + t*stride_t + h*stride_h
  *    (elements). Row outputs (y, h_out, dx / grad_h, dz) are dense
