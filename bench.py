@@ -219,15 +219,24 @@ def host_cpu():
 
 
 def cpu_sweep(out_md, reps=3):
-    """The FP64 oracle (single-threaded C) timed on every workload of the
-    configurations: each call runs on a sample of at most 2^24 elements of the
-    workload's rows (the oracle's cost is linear in the row count), median of
-    reps, scaled to the full row count. Writes a markdown table."""
+    """The FP64 oracle (plain C, unchanged) timed on every workload of the
+    configurations, on one thread and on every core (the sampled rows cut into
+    one block of tokens per core, each block a concurrent call of the same
+    single-threaded oracle): each call runs on a sample of at most 2^24
+    elements of the workload's rows (the oracle's cost is linear in the row
+    count), median of reps, scaled to the full row count. Writes a markdown
+    table."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import torch
 
     import oracle
     import synth
+
+    cores = host_cpu()["cpus_available"]
+    pool = ThreadPoolExecutor(cores)
+    oracle.lib()  # load (and, if stale, build) the library before anything is timed
 
     def bits(t):
         return t.contiguous().view(torch.int16).numpy().view(np.uint16)
@@ -242,16 +251,33 @@ def cpu_sweep(out_md, reps=3):
 
     rows_out = []
 
-    def add(cfg, workload, op, rows, sample_rows, dt, nbytes):
+    def add(cfg, workload, op, rows, sample_rows, dt, dtn, nbytes):
         us = dt * 1e6 * rows / sample_rows
-        rows_out.append((cfg, workload, op, sample_rows, dt, us, nbytes / (us * 1e-6) / 1e9))
-        print(f"[cpu] {cfg:3s} {workload:32s} {op:4s} {us:14.1f} us", file=sys.stderr, flush=True)
+        usn = dtn * 1e6 * rows / sample_rows
+        rows_out.append((cfg, workload, op, sample_rows, dt, us, nbytes / (us * 1e-6) / 1e9, usn,
+                         nbytes / (usn * 1e-6) / 1e9))
+        print(f"[cpu] {cfg:3s} {workload:32s} {op:4s} {us:14.1f} us  all cores {usn:12.1f} us",
+              file=sys.stderr, flush=True)
 
-    def views(p, form):
+    def views(p, form, t0=0, t1=None):
+        """The problem's views, or those of tokens [t0, t1) only."""
+        t1 = p.T if t1 is None else t1
+
         def v(buf):
-            return oracle.View(bits(buf), p.T, p.heads, p.width, p.row_stride, p.head_stride)
+            b = bits(buf)[t0 * p.row_stride:]
+            return oracle.View(b, t1 - t0, p.heads, p.width, p.row_stride, p.head_stride)
         return v(p.x), v(p.dy), (v(p.extra) if form != "plain" else None), \
             (v(p.dh) if form == "residual" else None)
+
+    def both(p, form, call):
+        """Median times of call(x, dy, e, dh) on all rows, and on one block of
+        tokens per core run concurrently."""
+        dt = med_time(lambda: call(*views(p, form)))
+        nb = min(cores, p.T)
+        cuts = [p.T * i // nb for i in range(nb + 1)]
+        blocks = [views(p, form, cuts[i], cuts[i + 1]) for i in range(nb)]
+        dtn = med_time(lambda: list(pool.map(lambda b: call(*b), blocks)))
+        return dt, dtn
 
     def run(cfg, T, W, heads=1, rs=None, hs=None, form="plain", w_dtype="f32", ops=("fwd", "bwd"),
             label=None):
@@ -259,31 +285,30 @@ def cpu_sweep(out_md, reps=3):
         ts = max(1, min(T, (1 << 24) // (W * heads)))
         p = synth.make(ts, W, seed=0, heads=heads, w_dtype=w_dtype, form=form, row_stride=rs,
                        head_stride=hs)
-        x, dy, e, dh = views(p, form)
         w = p.w.double().numpy()
         wb = 4 if w_dtype == "f32" else 2
         n, sr = rows * W, ts * heads
         name = label or f"[{T},{W}]"
         if "fwd" in ops:
             if form == "plain":
-                dt = med_time(lambda: oracle.fwd(x, w, p.eps))
-                add(cfg, name, "fwd", rows, sr, dt, 4 * n + 4 * rows + wb * W)
+                dt, dtn = both(p, form, lambda x, dy, e, dh: oracle.fwd(x, w, p.eps))
+                add(cfg, name, "fwd", rows, sr, dt, dtn, 4 * n + 4 * rows + wb * W)
             elif form == "residual":
-                dt = med_time(lambda: oracle.res_fwd(x, e, w, p.eps))
-                add(cfg, name, "fwd", rows, sr, dt, 8 * n + 4 * rows + wb * W)
+                dt, dtn = both(p, form, lambda x, dy, e, dh: oracle.res_fwd(x, e, w, p.eps))
+                add(cfg, name, "fwd", rows, sr, dt, dtn, 8 * n + 4 * rows + wb * W)
             else:
-                dt = med_time(lambda: oracle.gate_fwd(x, e, w, p.eps))
-                add(cfg, name, "fwd", rows, sr, dt, 6 * n + 4 * rows + wb * W)
+                dt, dtn = both(p, form, lambda x, dy, e, dh: oracle.gate_fwd(x, e, w, p.eps))
+                add(cfg, name, "fwd", rows, sr, dt, dtn, 6 * n + 4 * rows + wb * W)
         if "bwd" in ops:
             if form == "plain":
-                dt = med_time(lambda: oracle.bwd(dy, x, w, p.eps))
-                add(cfg, name, "bwd", rows, sr, dt, 6 * n + 4 * rows + wb * W + 4 * W)
+                dt, dtn = both(p, form, lambda x, dy, e, dh: oracle.bwd(dy, x, w, p.eps))
+                add(cfg, name, "bwd", rows, sr, dt, dtn, 6 * n + 4 * rows + wb * W + 4 * W)
             elif form == "residual":
-                dt = med_time(lambda: oracle.bwd(dy, x, w, p.eps, dh=dh))
-                add(cfg, name, "bwd", rows, sr, dt, 8 * n + 4 * rows + wb * W + 4 * W)
+                dt, dtn = both(p, form, lambda x, dy, e, dh: oracle.bwd(dy, x, w, p.eps, dh=dh))
+                add(cfg, name, "bwd", rows, sr, dt, dtn, 8 * n + 4 * rows + wb * W + 4 * W)
             else:
-                dt = med_time(lambda: oracle.gate_bwd(dy, x, e, w, p.eps))
-                add(cfg, name, "bwd", rows, sr, dt, 10 * n + 4 * rows + wb * W + 4 * W)
+                dt, dtn = both(p, form, lambda x, dy, e, dh: oracle.gate_bwd(dy, x, e, w, p.eps))
+                add(cfg, name, "bwd", rows, sr, dt, dtn, 10 * n + 4 * rows + wb * W + 4 * W)
 
     run("1", 8, 512, w_dtype="bf16")
     for W in (512, 1536, 2048, 4096, 5120, 6144):
@@ -296,20 +321,28 @@ def cpu_sweep(out_md, reps=3):
     run("4", 131072, 6144, form="residual", label="[131072,6144] residual")
     for T in (3534, 8192, 16384):
         run("5", T, 4096, form="gate", label=f"[{T},4096] gate")
+    pool.shutdown()
     host = host_cpu()
-    lines = ["# FP64 CPU oracle on every workload (single-threaded C)", "",
+    lines = ["# FP64 CPU oracle on every workload (one thread and all cores)", "",
              "Command (repository root $REPO, on the MI355X host; committed files only):", "",
              "```", "python3 $REPO/bench.py --cpu-sweep <this file>", "```", "",
-             f"Host: {host['model']}, {host['cpus_available']} logical CPUs available; the oracle "
-             "uses one thread (cores = 1). Each call runs on a sample of at most 2^24 elements "
-             f"of the workload's rows, median of {reps} runs, and is scaled to the full row count "
-             "(the oracle's cost is linear in the rows). GB/s uses the same algorithmic bytes as "
-             "the GPU tables: fwd 4TH, bwd 6TH, residual 8TH each way, gate fwd 6TH and bwd 10TH "
-             "(+ per-row and per-column terms).", "",
-             "| cfg | workload | op | rows timed | s per sample | us per full call | GB/s |",
-             "|---|---|---|---|---|---|---|"]
-    for cfg, wl, op, sr, dt, us, gbps in rows_out:
-        lines.append(f"| {cfg} | {wl} | {op} | {sr} | {dt:.4f} | {us:.1f} | {gbps:.3f} |")
+             f"Host: {host['model']} (lscpu: "
+             f"{'; '.join(f'{k} {v}' for k, v in host['lscpu'].items())}), "
+             f"{host['cpus_available']} logical CPUs "
+             "available. The oracle is the plain single-threaded C, unchanged: timed on one "
+             f"thread, and on all {cores} cores as one block of tokens per core, each block a "
+             "concurrent call of the same oracle (ctypes releases the GIL). Each call runs on a "
+             "sample of at most 2^24 elements of the workload's rows, median of "
+             f"{reps} runs, and is scaled to the full row count (the oracle's cost is linear in "
+             "the rows). GB/s uses the same algorithmic bytes as the GPU tables: fwd 4TH, bwd "
+             "6TH, residual 8TH each way, gate fwd 6TH and bwd 10TH (+ per-row and per-column "
+             "terms).", "",
+             "| cfg | workload | op | rows timed | s per sample (1 thread) | us per full call, 1 "
+             f"thread | GB/s, 1 thread | us per full call, {cores} cores | GB/s, {cores} cores |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for cfg, wl, op, sr, dt, us, gbps, usn, gbpsn in rows_out:
+        lines.append(f"| {cfg} | {wl} | {op} | {sr} | {dt:.4f} | {us:.1f} | {gbps:.3f} | "
+                     f"{usn:.1f} | {gbpsn:.3f} |")
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
