@@ -349,6 +349,7 @@ def cpu_sweep(out_md, reps=3):
 
 
 GATE_T = 16384  # gated form measured by the counter runs: [16384, 4096]
+SWEEP_REPS = 80  # calls per case and process in --sweep (the pages take 4 x 20 per process)
 
 
 def traffic_probe():
@@ -388,7 +389,7 @@ def traffic_probe():
     print("[bench] traffic probe done", file=sys.stderr, flush=True)
 
 
-def sweep(out_path, reps=20):
+def sweep(out_path, reps=SWEEP_REPS):
     """Every workload of the build, one graph-replayed call per timing with a
     512 MB write between calls (cold L2 and Infinity Cache). Writes a markdown
     table to out_path and returns the rows."""
@@ -622,7 +623,8 @@ def sweep_kernels(args, out_md):
            "Each call is one graph replay after a 512 MB read that evicts L2 and the Infinity Cache. "
            "Kernel-active span = first kernel start to last kernel end of the call (all of this "
            "library's kernels of the call: main + fold on the large path). The median and p10-p90 "
-           f"run over all calls of all {n} process{'es' if n > 1 else ''} (20 calls each); the "
+           f"run over all calls of all {n} process{'es' if n > 1 else ''} ({SWEEP_REPS} calls "
+           "each, the pages' 4 x 20 in one session); the "
            "per-process medians are the A/A check (the same case measured in another process, "
            "where the caching allocator may place the tensors elsewhere). The event column is "
            "the HIP-event time around the replay (median of the processes), which carries a ~13 "
