@@ -916,7 +916,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py: this benchmark runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by rows with one dw all-reduce; see the design notes)",
+              "(rows shard across GPUs with no exchange for the forward and dx and one "
+              "exchange of the FP64 dw per backward call; only one GPU is measured here)",
               file=sys.stderr)
         sys.exit(2)
 
