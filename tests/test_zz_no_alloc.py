@@ -95,3 +95,38 @@ def test_noalloc_rejects_what_the_workspace_entry_point_rejects():
                                        R.RMSN_F32, None, None)
     assert st == 9  # RMSN_E_ARG
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("det", [True, False], ids=["det", "nondet"])
+def test_noalloc_inside_a_graph_matches_eager(det):
+    # The callers this entry point is for include code under HIP graph
+    # capture: the captured call (outputs made before capture, through the C
+    # ABI) replays several times, with eager work on the same GPU in between,
+    # and every replay equals the eager call bit for bit.
+    T, H = 4099, 4096
+    x, dy, dh, w, rstd = _inputs(T, H, 7, torch.float32, residual=True)
+    L = R.Layout(T, 1, H, H, H, H, H)
+    dx = torch.empty_like(x)
+    dw = torch.empty(H, dtype=torch.float32, device=x.device)
+    ref = R.rmsnorm_train_bwd(dy, x, rstd, w, det, dh=dh)
+
+    def call(stream):
+        st = R.lib().rmsnorm_train_bwd_noalloc(
+            dy.data_ptr(), x.data_ptr(), dh.data_ptr(), w.data_ptr(), R.RMSN_F32,
+            rstd.data_ptr(), int(det), C.byref(L), dx.data_ptr(), dw.data_ptr(), R.RMSN_F32,
+            None, stream)
+        assert st == 0, R.lib().rmsn_status_str(st).decode()
+
+    call(torch.cuda.current_stream().cuda_stream)      # first call on this device, outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(torch.cuda.current_stream().cuda_stream)
+    for i in range(3):
+        dx.zero_()
+        dw.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        _compare((dx, dw), ref, det, f"replay {i}")    # bits in the deterministic mode
+        _ = R.rmsnorm_train_bwd(dy[:2000], x[:2000], rstd[:2000], w, det)   # eager work between
+        torch.cuda.synchronize()
