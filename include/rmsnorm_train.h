@@ -162,8 +162,8 @@ rmsn_status rmsnorm_train_fwd(const void* x, const void* residual, const void* w
  *   consecutive rows (R fixed per width) and the tiles are dealt in turn to K
  *   chunks: chunk k holds tiles k, k+K, k+2K, ... K depends only on T*heads
  *   and the width: ceil(tiles/8) when T*heads <= S, otherwise min(tiles,
- *   256), with S = 2048 at width 256, 1024 at 512, 768 at 1536 and 2048,
- *   640 at 4096, 512 at 5120 and 384 at 6144 (up to S rows the automatic
+ *   256), with S = 1280 at width 256, 960 at 512, 640 at 1536 and 2048,
+ *   512 at 4096 and 5120, and 384 at 6144 (up to S rows the automatic
  *   path is the single launch). Row q of each of a chunk's tiles,
  *   in ascending tile order, forms sub-chain q, summed with exact products
  *   (dy*x is exact in FP32, times rstd by an FMA-based TwoProduct) and

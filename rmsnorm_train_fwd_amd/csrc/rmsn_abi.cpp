@@ -28,11 +28,11 @@ constexpr int32_t kMaxGrid = 1 << 24;
 // as rows get wider. Both paths give the same bits for a given tree.
 int64_t small_rows(int64_t width) {
   switch (width) {
-    case 256: return 2048;
-    case 512: return 1024;
-    case 1536: return 768;
-    case 2048: return 768;
-    case 4096: return 640;
+    case 256: return 1280;
+    case 512: return 960;
+    case 1536: return 640;
+    case 2048: return 640;
+    case 4096: return 512;
     case 5120: return 512;
     default: return 384;  // 6144
   }

@@ -209,12 +209,12 @@ def query(T, W, heads=1, det=1, launch=None):
 
 
 SUBCHAINS = {256: 16, 512: 8, 1536: 4, 2048: 4, 4096: 2, 5120: 2, 6144: 1}
-SMALL_ROWS = {256: 2048, 512: 1024, 1536: 768, 2048: 768, 4096: 640, 5120: 512, 6144: 384}
+SMALL_ROWS = {256: 1280, 512: 960, 1536: 640, 2048: 640, 4096: 512, 5120: 512, 6144: 384}
 
 
 @pytest.mark.parametrize("W", [256, 512, 1536, 2048, 4096, 5120, 6144])
 @pytest.mark.parametrize("rows", [1, 15, 16, 17, 203, 256, 257, 300, 384, 385, 512, 513, 640, 641, 768, 769,
-                                  1024, 1025, 2048, 2049, 16384, 16385, 65537, 98304, 131072,
+                                  960, 961, 1024, 1025, 1280, 1281, 2048, 2049, 16384, 16385, 65537, 98304, 131072,
                                   113536, 786432, 3145728])
 def test_dw_tree_chunking(rows, W):
     p = query(rows, W)

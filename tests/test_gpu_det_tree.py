@@ -153,7 +153,7 @@ def test_det_dw_bits_follow_the_documented_tree_under_cancellation(H, rows, path
 
 # Row counts where the tree switches from at most 8 tiles per chunk (and the
 # single-launch path) to up to 256 chunks (main kernel + fold): S(width).
-SMALL_ROWS = {256: 2048, 512: 1024, 1536: 768, 2048: 768, 4096: 640, 5120: 512, 6144: 384}
+SMALL_ROWS = {256: 1280, 512: 960, 1536: 640, 2048: 640, 4096: 512, 5120: 512, 6144: 384}
 
 
 @pytest.mark.parametrize("path", [R.PATH_LARGE, R.PATH_SMALL], ids=["large", "small"])
