@@ -348,14 +348,14 @@ def cpu_sweep(out_md, reps=3):
     print("\n".join(lines))
 
 
-GATE_T = 16384  # gated form measured by the counter runs: [16384, 4096]
+GATE_TS = (16384, 8192, 3534)  # gated form measured by the counter runs: [T, 4096], in this order
 SWEEP_REPS = 80  # calls per case and process in --sweep (the pages take 4 x 20 per process)
 
 
 def traffic_probe():
     """For rocprofv3 --pmc runs: one plain copy of known size (calibration),
     then three forward and three backward calls at the headline shape, and
-    three gated forward and backward calls at [16384, 4096]."""
+    three gated forward and backward calls at each of [16384 | 8192 | 3534, 4096]."""
     import torch
 
     import rmsnorm_train_fwd_amd as R
@@ -378,14 +378,16 @@ def traffic_probe():
         R.rmsnorm_train_bwd(dy, x, rstd, w, False)
     torch.cuda.synchronize()
     del x, dy, rstd
-    g = synth.make(GATE_T, H_HEAD, seed=0, w_dtype="f32", form="gate")
-    x, z = g.x.to(dev).view(GATE_T, H_HEAD), g.extra.to(dev).view(GATE_T, H_HEAD)
-    dy, w = g.dy.to(dev).view(GATE_T, H_HEAD), g.w.to(dev)
-    for _ in range(3):
-        _, rstd = R.rmsnorm_silu_gate_train_fwd(x, z, w, g.eps)
-    for _ in range(3):
-        R.rmsnorm_silu_gate_train_bwd(dy, x, z, rstd, w, False)
-    torch.cuda.synchronize()
+    for T in GATE_TS:
+        g = synth.make(T, H_HEAD, seed=0, w_dtype="f32", form="gate")
+        x, z = g.x.to(dev).view(T, H_HEAD), g.extra.to(dev).view(T, H_HEAD)
+        dy, w = g.dy.to(dev).view(T, H_HEAD), g.w.to(dev)
+        for _ in range(3):
+            _, rstd = R.rmsnorm_silu_gate_train_fwd(x, z, w, g.eps)
+        for _ in range(3):
+            R.rmsnorm_silu_gate_train_bwd(dy, x, z, rstd, w, False)
+        torch.cuda.synchronize()
+        del x, z, dy, w, rstd
     print("[bench] traffic probe done", file=sys.stderr, flush=True)
 
 
@@ -709,7 +711,7 @@ def traffic_report(fetch_dir, write_dir, out_json, out_md):
 
     def load(d):
         f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
-        return list(csv.DictReader(open(f)))
+        return sorted(csv.DictReader(open(f)), key=lambda r: int(r["Dispatch_Id"]))
 
     F, W = load(fetch_dir), load(write_dir)
     GiB = 1 << 30
@@ -721,8 +723,14 @@ def traffic_report(fetch_dir, write_dir, out_json, out_md):
 
     ff, wf = GiB / (copy_kib(F) * 1024), GiB / (copy_kib(W) * 1024)
 
-    def per(rows, key, factor):
+    def per(rows, key, factor, part=None):
+        """Mean bytes per dispatch of the kernels whose name holds key; part =
+        (i, n): the i-th of n equal consecutive groups of those dispatches."""
         v = [float(r["Counter_Value"]) * 1024 * factor for r in rows if key in r["Kernel_Name"]]
+        if part is not None:
+            i, n = part
+            m = len(v) // n
+            v = v[i * m:(i + 1) * m]
         return sum(v) / len(v)
 
     plain_bwd = f"k_bwd_large<{H_HEAD}, true, 0, false"
@@ -730,15 +738,28 @@ def traffic_report(fetch_dir, write_dir, out_json, out_md):
     plain_fwd, gate_fwd = f"k_fwd<{H_HEAD}, true, 0,", f"k_fwd<{H_HEAD}, true, 2,"
     gate_bwd = f"k_bwd_large<{H_HEAD}, true, 2, false"
     fwr, fww = per(F, plain_fwd, ff), per(W, plain_fwd, wf)
-    gfr, gfw = per(F, gate_fwd, ff), per(W, gate_fwd, wf)
-    gbr, gbw = per(F, gate_bwd, ff), per(W, gate_bwd, wf)
-    TH, GH = T_HEAD * H_HEAD, GATE_T * H_HEAD
     alg_fwd = fwd_bytes(T_HEAD, H_HEAD, 4)
-    alg_gf, alg_gb = 6 * GH + 4 * GATE_T + 4 * H_HEAD, 10 * GH + 4 * GATE_T + 8 * H_HEAD
     import torch
     import rmsnorm_train_fwd_amd as R
-    chunks = R.rmsnorm_train_bwd_query(torch.empty((T_HEAD, H_HEAD), dtype=torch.bfloat16), False).chunks
+
+    def chunks_of(T):
+        return R.rmsnorm_train_bwd_query(torch.empty((T, H_HEAD), dtype=torch.bfloat16),
+                                         False).chunks
+
+    chunks = chunks_of(T_HEAD)
+    # every backward call above ends with one fold; at these shapes all of
+    # them fold the same 256 x 4096 partials
     fr, fw = per(F, "k_fold", ff), per(W, "k_fold", wf)
+    gate = []
+    for i, T in enumerate(GATE_TS):
+        GH = T * H_HEAD
+        part = (i, len(GATE_TS))
+        gfr, gfw = per(F, gate_fwd, ff, part), per(W, gate_fwd, wf, part)
+        gbr, gbw = per(F, gate_bwd, ff, part), per(W, gate_bwd, wf, part)
+        alg_gf, alg_gb = 6 * GH + 4 * T + 4 * H_HEAD, 10 * GH + 4 * T + 8 * H_HEAD
+        part_b = 2 * chunks_of(T) * H_HEAD * 8  # partials written by the main kernel, read by the fold
+        gate.append(dict(T=T, fr=gfr, fw=gfw, br=gbr, bw=gbw, alg_f=alg_gf, alg_b=alg_gb,
+                         partials=part_b))
     total, alg = kr + kw + fr + fw, bwd_bytes(T_HEAD, H_HEAD, 4)
     out = {"kernel_hash": kernel_hash(),
            "workload": "rmsnorm_train_bwd non-deterministic [131072,4096] BF16, w FP32",
@@ -749,16 +770,30 @@ def traffic_report(fetch_dir, write_dir, out_json, out_md):
            "forward": {"workload": "rmsnorm_train_fwd [131072,4096] BF16, w FP32",
                        "read": round(fwr), "write": round(fww), "algorithmic": alg_fwd,
                        "ratio_to_algorithmic": round((fwr + fww) / alg_fwd, 5)},
-           "gate_forward": {"workload": "rmsnorm_silu_gate_train_fwd [16384,4096] BF16, w FP32",
-                            "read": round(gfr), "write": round(gfw), "algorithmic": alg_gf,
-                            "ratio_to_algorithmic": round((gfr + gfw) / alg_gf, 5)},
-           "gate_backward_main": {"workload": "rmsnorm_silu_gate_train_bwd non-deterministic "
-                                  "[16384,4096] BF16, w FP32 (main kernel; k_fold as above)",
-                                  "read": round(gbr), "write": round(gbw), "algorithmic": alg_gb,
-                                  "ratio_to_algorithmic": round((gbr + gbw) / alg_gb, 5)},
+           "gate": [{"T": g["T"], "width": H_HEAD, "w": "FP32",
+                     "forward": {"read": round(g["fr"]), "write": round(g["fw"]),
+                                 "algorithmic": g["alg_f"],
+                                 "ratio_to_algorithmic": round((g["fr"] + g["fw"]) / g["alg_f"], 5)},
+                     "backward": {"read": round(g["br"] + fr), "write": round(g["bw"] + fw),
+                                  "algorithmic": g["alg_b"],
+                                  "ratio_to_algorithmic":
+                                      round((g["br"] + g["bw"] + fr + fw) / g["alg_b"], 5),
+                                  "fp64_partials_round_trip": g["partials"]}}
+                    for g in gate],
            "calibration_kib": {"fetch": copy_kib(F), "write": copy_kib(W)}}
     with open(out_json, "w") as fh:
         json.dump(out, fh, indent=1)
+    gate_rows = "\n".join(
+        f"| k_fwd<4096, w FP32, gate> [{g['T']}, 4096] | {g['fr'] / 1e9:.4f} GB | "
+        f"{g['fw'] / 1e9:.4f} GB |\n"
+        f"| k_bwd_large<4096, w FP32, gate, non-det> [{g['T']}, 4096] | {g['br'] / 1e9:.4f} GB | "
+        f"{g['bw'] / 1e9:.4f} GB |" for g in gate)
+    gate_table = "\n".join(
+        f"| {g['T']} | {g['alg_f'] / 1e6:.1f} MB | {(g['fr'] + g['fw']) / 1e6:.1f} MB "
+        f"({100 * ((g['fr'] + g['fw']) / g['alg_f'] - 1):+.2f}%) | {g['alg_b'] / 1e6:.1f} MB | "
+        f"{(g['br'] + g['bw'] + fr + fw) / 1e6:.1f} MB "
+        f"({100 * ((g['br'] + g['bw'] + fr + fw) / g['alg_b'] - 1):+.2f}%) | "
+        f"{g['partials'] / 1e6:.1f} MB ({100 * g['partials'] / g['alg_b']:.1f}%) |" for g in gate)
     md = f"""# HBM traffic of the backward call at [131072, 4096] (rocprofv3 counters)
 
 Commands (repository root $REPO, output directory $OUT, on an MI355X; committed files only; one counter per run):
@@ -772,7 +807,8 @@ python3 $REPO/bench.py --traffic-report $OUT/pmc_fetch $OUT/pmc_write <json> <th
 
 `bench.py --traffic-probe` runs one 1 GiB device-to-device copy (torch `copy_`, dispatched as
 `__amd_rocclr_copyBuffer`), the forward and the non-deterministic backward three times each at
-[131072, 4096], then the gated forward and backward three times each at [16384, 4096].
+[131072, 4096], then the gated forward and backward three times each at [16384, 4096],
+[8192, 4096] and [3534, 4096] (dispatches told apart by their order).
 Calibration with that copy of known size (1 GiB read, 1 GiB written): FETCH_SIZE read
 {copy_kib(F):.1f} KiB and WRITE_SIZE {copy_kib(W):.1f} KiB, so read bytes = FETCH_SIZE x 1024 x
 {ff:.5f} and written bytes = WRITE_SIZE x 1024 x {wf:.5f}.
@@ -783,8 +819,7 @@ Calibration with that copy of known size (1 GiB read, 1 GiB written): FETCH_SIZE
 | k_fold | {fr / 1e9:.4f} GB | {fw / 1e6:.3f} MB |
 | **backward call** | **{(kr + fr) / 1e9:.4f} GB** | **{(kw + fw) / 1e9:.4f} GB** |
 | k_fwd<4096, w FP32, plain> [131072, 4096] | {fwr / 1e9:.4f} GB | {fww / 1e9:.4f} GB |
-| k_fwd<4096, w FP32, gate> [16384, 4096] | {gfr / 1e9:.4f} GB | {gfw / 1e9:.4f} GB |
-| k_bwd_large<4096, w FP32, gate, non-det> [16384, 4096] | {gbr / 1e9:.4f} GB | {gbw / 1e9:.4f} GB |
+{gate_rows}
 
 Algorithmic: reads x, dy, rstd, w = {(4 * T_HEAD * H_HEAD + 4 * T_HEAD + 4 * H_HEAD) / 1e9:.4f} GB;
 writes dx, dw = {(2 * T_HEAD * H_HEAD + 4 * H_HEAD) / 1e9:.4f} GB; total {alg / 1e9:.4f} GB.
@@ -792,11 +827,14 @@ Measured {total / 1e9:.4f} GB per call, {100 * (total / alg - 1):.2f}% above it:
 partials ({chunks} x {H_HEAD} x 8 B = {chunks * H_HEAD * 8 / 2**20:.0f} MiB) written by the main kernel and read back by the fold.
 Forward at [131072, 4096]: algorithmic x read, y and rstd written, w read =
 {alg_fwd / 1e9:.4f} GB; measured {(fwr + fww) / 1e9:.4f} GB ({100 * ((fwr + fww) / alg_fwd - 1):+.2f}%).
-Gated form at [16384, 4096]: forward algorithmic (x, z read; y, rstd written; w) {alg_gf / 1e9:.4f} GB,
-measured {(gfr + gfw) / 1e9:.4f} GB ({100 * ((gfr + gfw) / alg_gf - 1):+.2f}%); backward main kernel
-algorithmic (x, dy, z, rstd, w read; dx, dz written; dw) {alg_gb / 1e9:.4f} GB, measured
-{(gbr + gbw) / 1e9:.4f} GB ({100 * ((gbr + gbw) / alg_gb - 1):+.2f}%, its chunk partials included).
-x, dy and dx are each moved once. Kernel sources hash: {out['kernel_hash']} (bench.py reports
+Gated form (forward: x, z read, y, rstd written, w; backward: x, dy, z, rstd, w read, dx, dz
+written, dw), per call, the backward being main kernel + fold:
+
+| gated [T, 4096] | fwd algorithmic | fwd measured | bwd algorithmic | bwd measured | FP64 partials written + read back |
+|---|---|---|---|---|---|
+{gate_table}
+
+At the headline shape x, dy and dx are each moved once. Kernel sources hash: {out['kernel_hash']} (bench.py reports
 `traffic` only while the current sources hash to this value).
 """
     with open(out_md, "w") as fh:
