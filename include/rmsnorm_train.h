@@ -194,8 +194,9 @@ rmsn_status rmsnorm_train_bwd(const void* dy, const void* x, const void* dh, con
  * largest any plan needs), held by each GPU the library runs on until the
  * process ends; a plan needing more would return RMSN_E_WORKSPACE. The call
  * uses the array of the calling thread's current HIP device, so `stream` must
- * belong to that device; the first call on a device looks up the array's
- * address there (RMSN_E_HIP if that fails). It calls no allocator.
+ * belong to that device (a stream of another device: RMSN_E_ARG, nothing
+ * enqueued); the first call on a device looks up the array's address there
+ * (RMSN_E_HIP if that fails). It calls no allocator.
  * Every call on one GPU shares that GPU's array, which keeps the last call's
  * contents (nothing in it needs clearing). Calls that can overlap in time on
  * one GPU (unordered streams, several host threads) race on the array and

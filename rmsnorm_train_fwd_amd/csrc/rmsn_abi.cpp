@@ -200,7 +200,7 @@ rmsn_status bwd_common(int form, const void* dy, const void* x, const void* e, c
   rmsn_bwd_plan plan;
   make_plan(*L, det, o, &plan);
   if (ws_source && plan.workspace_bytes > 0) {
-    if ((st = ws_source(plan.workspace_bytes, &ws, &ws_bytes))) return st;
+    if ((st = ws_source(stream, plan.workspace_bytes, &ws, &ws_bytes))) return st;
   }
   if (plan.workspace_bytes > 0) {
     if (!ws || ws_bytes < plan.workspace_bytes) return RMSN_E_WORKSPACE;

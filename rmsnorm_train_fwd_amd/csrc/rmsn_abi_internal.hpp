@@ -22,10 +22,11 @@ inline int enum_code(const E& e) {
   return v;
 }
 
-// Supplies the workspace of a backward call once validation and planning have
-// passed and the plan needs `need` bytes: sets *ws and *ws_bytes, or returns
-// the status the call then returns (nothing has been enqueued yet).
-typedef rmsn_status (*WorkspaceSource)(size_t need, void** ws, size_t* ws_bytes);
+// Supplies the workspace of a backward call on `stream` once validation and
+// planning have passed and the plan needs `need` bytes: sets *ws and
+// *ws_bytes, or returns the status the call then returns (nothing has been
+// enqueued yet).
+typedef rmsn_status (*WorkspaceSource)(void* stream, size_t need, void** ws, size_t* ws_bytes);
 
 // The backward of every form (kPlain, kResidual, kGate): validation, plan,
 // launches. With ws_source NULL the caller's (ws, ws_bytes) is the workspace;

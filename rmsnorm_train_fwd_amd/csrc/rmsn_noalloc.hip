@@ -33,11 +33,18 @@ std::mutex g_mu;
 void* g_scratch[kMaxDevices];  // device address of `scratch` per device, once looked up
 
 // Workspace source of the no-allocation entry point: the current device's
-// `scratch`, looked up on the first call on that device.
-rmsn_status scratch_source(size_t need, void** ws, size_t* ws_bytes) {
+// `scratch`, looked up on the first call on that device. A stream of another
+// device is refused (its kernels would reach this device's array).
+rmsn_status scratch_source(void* stream, size_t need, void** ws, size_t* ws_bytes) {
   if (need > kScratchBytes) return RMSN_E_WORKSPACE;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RMSN_E_HIP;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess)
+      return RMSN_E_HIP;
+    if (sdev != dev) return RMSN_E_ARG;
+  }
   std::lock_guard<std::mutex> lock(g_mu);
   if (!g_scratch[dev]) {
     void* p = nullptr;
