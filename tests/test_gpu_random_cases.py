@@ -3,15 +3,20 @@
 input family and a forced path, all drawn from one fixed generator, so the
 cases are the same on every run. Each case runs the forward and both backward
 modes and checks every row and column against the FP64 oracle within the same
-budgets as the configuration tests. The shapes are small enough for the
-oracle to take well under a second each.
+budgets as the configuration tests; a second test requires the deterministic
+dw and dx to keep their bits under three drawn launch overrides (grids of both
+launches, either path), as the deterministic mode promises (PR #8512 page,
+description). The shapes are small enough for the oracle to take well under a
+second each.
 """
 import numpy as np
 import pytest
+import torch
 
 import rmsnorm_train_fwd_amd as R
 import synth
 
+from helpers import OnGpu, bits
 from test_gpu_parity import run_case
 
 pytestmark = pytest.mark.gpu
@@ -36,8 +41,13 @@ def draw_cases(n=N_CASES, seed=20261203):
         zero_centred = bool(rng.random() < 0.2)
         family = str(rng.choice(["normal", "normal", "spread"]))
         path = int(rng.choice([R.PATH_AUTO, R.PATH_AUTO, R.PATH_SMALL, R.PATH_LARGE]))
+        # launch overrides for the bitwise check: (grid, fold grid, path)
+        launches = [(int(rng.choice([0, 1, rng.integers(2, 5000)])),
+                     int(rng.choice([0, 1, rng.integers(2, 300)])),
+                     int(rng.choice([R.PATH_SMALL, R.PATH_LARGE]))) for _ in range(3)]
         cases.append(dict(i=i, W=W, form=form, heads=heads, T=T, hs=hs, rs=rs, w_dtype=w_dtype,
-                          zero_centred=zero_centred, family=family, path=path))
+                          zero_centred=zero_centred, family=family, path=path,
+                          launches=launches))
     return cases
 
 
@@ -51,13 +61,55 @@ def test_the_draw_covers_every_width_form_and_path():
     assert any(c["heads"] > 1 for c in CASES) and any(c["zero_centred"] for c in CASES)
 
 
-@pytest.mark.parametrize("c", CASES, ids=lambda c: (f"{c['i']}-{c['form']}-[{c['T']},{c['heads']},"
-                                                     f"{c['W']}]-{c['w_dtype']}"))
+def _problem(c):
+    return synth.make(c["T"], c["W"], seed=c["i"], heads=c["heads"], w_dtype=c["w_dtype"],
+                      family=c["family"], form=c["form"], row_stride=c["rs"],
+                      head_stride=c["hs"] if c["heads"] > 1 else None,
+                      w_centre=0.0 if c["zero_centred"] else 1.0)
+
+
+def _ids(c):
+    return f"{c['i']}-{c['form']}-[{c['T']},{c['heads']},{c['W']}]-{c['w_dtype']}"
+
+
+@pytest.mark.parametrize("c", CASES, ids=_ids)
 def test_random_case_matches_the_oracle(c):
-    p = synth.make(c["T"], c["W"], seed=c["i"], heads=c["heads"], w_dtype=c["w_dtype"],
-                   family=c["family"], form=c["form"], row_stride=c["rs"],
-                   head_stride=c["hs"] if c["heads"] > 1 else None,
-                   w_centre=0.0 if c["zero_centred"] else 1.0)
     launch = None if c["path"] == R.PATH_AUTO else R.Launch(0, 0, c["path"])
-    run_case(p, det=(True, False), form=c["form"], launch=launch,
+    run_case(_problem(c), det=(True, False), form=c["form"], launch=launch,
              zero_centred=c["zero_centred"])
+
+
+def _det_bwd(g, c, rstd, h, launch):
+    zc = dict(zero_centred=c["zero_centred"])
+    if c["form"] == "residual":
+        dx, dw = R.rmsnorm_train_bwd(g.dy, h, rstd, g.w, True, dh=g.dh, launch=launch, **zc)
+        return bits(dx), dw.cpu().numpy().view(np.uint32)
+    if c["form"] == "gate":
+        dx, dz, dw = R.rmsnorm_silu_gate_train_bwd(g.dy, g.x, g.e, rstd, g.w, True,
+                                                   launch=launch, **zc)
+        return (np.concatenate([bits(dx).ravel(), bits(dz).ravel()]),
+                dw.cpu().numpy().view(np.uint32))
+    dx, dw = R.rmsnorm_train_bwd(g.dy, g.x, rstd, g.w, True, launch=launch, **zc)
+    return bits(dx), dw.cpu().numpy().view(np.uint32)
+
+
+@pytest.mark.parametrize("c", CASES, ids=_ids)
+def test_random_case_det_bits_do_not_depend_on_the_launch(c):
+    # the deterministic dw and dx keep their bits under three drawn launch
+    # overrides (workgroup counts of both launches, either path)
+    g = OnGpu(_problem(c))
+    zc = dict(zero_centred=c["zero_centred"])
+    h = None
+    if c["form"] == "residual":
+        _, rstd, h = R.rmsnorm_train_fwd(g.x, g.w, residual=g.e, **zc)
+    elif c["form"] == "gate":
+        _, rstd = R.rmsnorm_silu_gate_train_fwd(g.x, g.e, g.w, **zc)
+    else:
+        _, rstd = R.rmsnorm_train_fwd(g.x, g.w, **zc)
+    ref_dx, ref_dw = _det_bwd(g, c, rstd, h, None)
+    for grid, fold_grid, path in c["launches"]:
+        dx, dw = _det_bwd(g, c, rstd, h, R.Launch(grid, fold_grid, path))
+        tag = (grid, fold_grid, path)
+        assert np.array_equal(dw, ref_dw), f"det dw bits changed with launch {tag}"
+        assert np.array_equal(dx, ref_dx), f"dx bits changed with launch {tag}"
+    torch.cuda.synchronize()
