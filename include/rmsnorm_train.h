@@ -50,6 +50,12 @@
  *    (elements). Row outputs (y, h_out, dx / grad_h, dz) are dense
  *    [T, heads, width]; rstd is dense [T*heads]; dw is [width].
  *  - Supported widths: 256, 512, 1536, 2048, 4096, 5120, 6144 ([C]).
+ *  - Sizes: T >= 0, heads >= 1, T*heads <= 2^31 - 1 rows, and each view's
+ *    extent (last element + 1, in bytes) at most 2^48 (else RMSN_E_SHAPE).
+ *  - Strides, for each pair (x_*, g_*): with heads > 1, width <= stride_h <=
+ *    2^40; with T > 1, (heads - 1)*stride_h + width <= stride_t <= 2^40, i.e.
+ *    rows never overlap (else RMSN_E_STRIDE). A stride whose dimension has
+ *    size 1 is not used and not checked.
  *  - Alignment: every BF16 row pointer, w and dw 16-byte aligned; strides
  *    multiples of 8 elements; rstd 4-byte aligned; workspace 16-byte aligned.
  *  - Overlap: no output may share a byte with an input or another output

@@ -88,7 +88,8 @@ rmsn_status check_layout(const rmsn_layout* L) {
       if (sh % 8) return RMSN_E_ALIGN;
     }
     if (L->T > 1) {
-      const int64_t need = (L->heads - 1) * (L->heads > 1 ? sh : 0) + L->width;
+      // wide: (heads - 1) * stride_h can exceed 64 bits within the bounds above
+      const __int128 need = (__int128)(L->heads - 1) * (L->heads > 1 ? sh : 0) + L->width;
       if (st < need || st > kMaxStride) return RMSN_E_STRIDE;
       if (st % 8) return RMSN_E_ALIGN;
     }

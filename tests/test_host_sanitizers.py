@@ -28,8 +28,8 @@ HIPCC = libbuild.HIPCC
 RUNTIME = sorted(glob.glob(f"{LLVM}/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
 HOST_SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
-TESTS = ["tests/test_abi_host.py", "tests/test_binding_checks.py", "tests/test_golden.py",
-         "tests/test_oracle_pins.py"]
+TESTS = ["tests/test_abi_host.py", "tests/test_abi_fuzz.py", "tests/test_binding_checks.py",
+         "tests/test_golden.py", "tests/test_oracle_pins.py"]
 
 
 def _gpu_visible() -> bool:
