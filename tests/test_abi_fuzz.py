@@ -155,3 +155,132 @@ def test_huge_head_count_with_the_largest_head_stride_is_rejected():
     W, heads, sh = 256, 2**30 - 1, 2**40
     rc, _ = query(2, heads, W, (2**40, sh), (2**40, sh))
     assert rc == E_STRIDE
+
+
+# ---------------------------------------------------------------- backward call --
+#
+# Fake device addresses (never dereferenced: validation runs on the host and a
+# call that passes it returns RMSN_E_HIP here, where no GPU is visible). Each
+# buffer gets its own 1 MiB-aligned region; a draw may then move an output into
+# another buffer's extent, misalign a pointer, or drop it.
+
+def _extent(T, heads, W, s_t, s_h):
+    if T == 0:
+        return 0
+    last = ((T - 1) * s_t if T > 1 else 0) + ((heads - 1) * s_h if heads > 1 else 0) + W
+    return 2 * last
+
+
+def _overlap(a, b):
+    (pa, na), (pb, nb) = a, b
+    return pa is not None and pb is not None and na > 0 and nb > 0 and pa < pb + nb and pb < pa + na
+
+
+@st.composite
+def bwd_calls(draw):
+    T, heads, W, xs, gs = draw(valid_layouts().filter(lambda l: l[0] * l[1] <= 20000))
+    form = draw(st.sampled_from(["plain", "residual", "gate"]))
+    wd = draw(st.sampled_from([0, 1, 2, 3, 0, 1, 4, -1]))
+    dwd = draw(st.sampled_from([0, 1, 0, 1, 2]))
+    det = draw(st.sampled_from([0, 1, 0, 1, 2]))
+    rows = T * heads
+    w_bytes = W * (4 if wd in (1, 3) else 2)
+    sizes = {
+        "dy": _extent(T, heads, W, *gs), "x": _extent(T, heads, W, *xs),
+        "e": (_extent(T, heads, W, *gs) if form == "residual" else _extent(T, heads, W, *xs))
+        if form != "plain" else 0,
+        "w": w_bytes, "rstd": 4 * rows, "dx": 2 * rows * W,
+        "dz": 2 * rows * W if form == "gate" else 0, "dw": W * (4 if dwd == 1 else 2),
+    }
+    ptr = {k: (1 + i) << 40 for i, k in enumerate(sizes)}
+    if form == "plain":
+        ptr["e"] = None
+    if form != "gate":
+        ptr["dz"] = None
+    ws_need = None
+    rc, plan = query(T, heads, W, xs, gs, det=det if det in (0, 1) else 1)
+    ws_need = plan.workspace_bytes if rc == OK else 0
+    ws = (20 << 40) if ws_need else None
+    ws_bytes = ws_need
+    # perturbations
+    for _ in range(draw(st.integers(0, 2))):
+        kind = draw(st.sampled_from(["null", "misalign", "alias", "ws_small", "ws_null"]))
+        key = draw(st.sampled_from(sorted(sizes)))
+        if kind == "null" and ptr.get(key) is not None:
+            ptr[key] = None
+        elif kind == "misalign" and ptr.get(key) is not None:
+            ptr[key] += draw(st.sampled_from([2, 4, 8]))
+        elif kind == "alias":
+            out = draw(st.sampled_from(["dx", "dz", "dw"]))
+            if ptr.get(out) is not None and ptr.get(key) is not None and sizes[key] > 0:
+                ptr[out] = ptr[key] + 16 * draw(st.integers(0, max(0, sizes[key] // 16 - 1)))
+        elif kind == "ws_small" and ws_need:
+            ws_bytes = draw(st.integers(0, ws_need - 1))
+        elif kind == "ws_null" and ws_need:
+            ws = None
+    return dict(T=T, heads=heads, W=W, xs=xs, gs=gs, form=form, wd=wd, dwd=dwd, det=det,
+                sizes=sizes, ptr=ptr, ws=ws, ws_bytes=ws_bytes, ws_need=ws_need)
+
+
+def bwd_broken_rules(c):
+    """Codes of the header rules a backward call breaks (the layout is valid)."""
+    bad = set()
+    p, n = c["ptr"], c["sizes"]
+    rows = c["T"] * c["heads"]
+    gate = c["form"] == "gate"
+    if c["wd"] not in (0, 1, 2, 3) or c["dwd"] not in (0, 1):
+        bad.add(E_DTYPE)
+    if c["det"] not in (0, 1):
+        bad.add(E_ARG)
+    if p["w"] is None or p["dw"] is None:
+        bad.add(E_NULL)
+    if rows > 0:
+        if any(p[k] is None for k in ("dy", "x", "rstd", "dx")):
+            bad.add(E_NULL)
+        if gate and (p["e"] is None or p["dz"] is None):
+            bad.add(E_NULL)
+        if c["form"] == "residual" and p["e"] is None:
+            pass  # dh NULL selects the plain form: no rule broken by itself
+    al16 = [k for k in ("w", "dw") if p[k] is not None and p[k] % 16]
+    if rows > 0:
+        al16 += [k for k in ("dy", "x", "dx", "e", "dz") if p.get(k) is not None and p[k] % 16]
+        if p["rstd"] is not None and p["rstd"] % 4:
+            al16.append("rstd")
+    if al16:
+        bad.add(E_ALIGN)
+    if c["ws_need"]:
+        if c["ws"] is None or c["ws_bytes"] < c["ws_need"]:
+            bad.add(E_WS)
+    # overlaps: outputs against inputs and each other
+    ins = [(p[k], n[k]) for k in ("dy", "x", "e", "w", "rstd")]
+    outs = [(p[k], n[k]) for k in ("dx", "dz", "dw")] + [(c["ws"], c["ws_need"] if c["ws"] else 0)]
+    for i, o in enumerate(outs):
+        if any(_overlap(o, b) for b in ins) or any(_overlap(o, b) for j, b in enumerate(outs) if j != i):
+            bad.add(E_ALIAS)
+    return bad
+
+
+@settings(max_examples=800, deadline=None, suppress_health_check=[HealthCheck.too_slow,
+                                                                   HealthCheck.filter_too_much])
+@given(bwd_calls())
+def test_bwd_call_status_follows_the_header_rules(c):
+    import torch
+    if torch.cuda.is_available():
+        return  # a valid call would launch on fake addresses
+    p = c["ptr"]
+    L = R.Layout(c["T"], c["heads"], c["W"], c["xs"][0], c["xs"][1], c["gs"][0], c["gs"][1])
+    args = (p["dy"], p["x"])
+    if c["form"] == "gate":
+        rc = R.lib().rmsnorm_silu_gate_train_bwd(p["dy"], p["x"], p["e"], p["w"], c["wd"], p["rstd"],
+                                                  c["det"], C.byref(L), p["dx"], p["dz"], p["dw"],
+                                                  c["dwd"], c["ws"], c["ws_bytes"], None, None)
+    else:
+        dh = p["e"] if c["form"] == "residual" else None
+        rc = R.lib().rmsnorm_train_bwd(*args, dh, p["w"], c["wd"], p["rstd"], c["det"], C.byref(L),
+                                       p["dx"], p["dw"], c["dwd"], c["ws"], c["ws_bytes"], None,
+                                       None)
+    bad = bwd_broken_rules(c)
+    if bad:
+        assert rc in bad, f"status {rc}, broken rules {sorted(bad)}"
+    else:
+        assert rc == E_HIP, f"status {rc} for a call that breaks no rule"
