@@ -284,3 +284,95 @@ def test_bwd_call_status_follows_the_header_rules(c):
         assert rc in bad, f"status {rc}, broken rules {sorted(bad)}"
     else:
         assert rc == E_HIP, f"status {rc} for a call that breaks no rule"
+
+
+# ----------------------------------------------------------------- forward call --
+
+@st.composite
+def fwd_calls(draw):
+    T, heads, W, xs, _ = draw(valid_layouts().filter(lambda l: l[0] * l[1] <= 20000))
+    form = draw(st.sampled_from(["plain", "residual", "gate"]))
+    wd = draw(st.sampled_from([0, 1, 2, 3, 0, 1, 5]))
+    eps = draw(st.sampled_from([1e-6, 0.0, 1e-5, -1e-6, float("nan"), float("inf")]))
+    rows = T * heads
+    sizes = {"x": _extent(T, heads, W, *xs), "e": _extent(T, heads, W, *xs) if form != "plain" else 0,
+             "w": W * (4 if wd in (1, 3) else 2), "y": 2 * rows * W,
+             "h": 2 * rows * W if form == "residual" else 0, "rstd": 4 * rows}
+    ptr = {k: (1 + i) << 40 for i, k in enumerate(sizes)}
+    if form == "plain":
+        ptr["e"] = None
+    if form != "residual":
+        ptr["h"] = None
+    if form == "plain" and draw(st.integers(0, 9)) == 0:
+        ptr["h"] = 7 << 40  # h_out without a residual
+    for _ in range(draw(st.integers(0, 2))):
+        kind = draw(st.sampled_from(["null", "misalign", "alias"]))
+        key = draw(st.sampled_from(sorted(sizes)))
+        if kind == "null" and ptr.get(key) is not None:
+            ptr[key] = None
+        elif kind == "misalign" and ptr.get(key) is not None:
+            ptr[key] += draw(st.sampled_from([2, 4, 8]))
+        elif kind == "alias":
+            out = draw(st.sampled_from(["y", "h", "rstd"]))
+            if ptr.get(out) is not None and ptr.get(key) is not None and sizes[key] > 0:
+                ptr[out] = ptr[key] + 16 * draw(st.integers(0, max(0, sizes[key] // 16 - 1)))
+    return dict(T=T, heads=heads, W=W, xs=xs, form=form, wd=wd, eps=eps, sizes=sizes, ptr=ptr)
+
+
+def fwd_broken_rules(c):
+    bad = set()
+    p, n = c["ptr"], c["sizes"]
+    rows = c["T"] * c["heads"]
+    gate = c["form"] == "gate"
+    if c["wd"] not in (0, 1, 2, 3):
+        bad.add(E_DTYPE)
+    if not (c["eps"] >= 0.0 and c["eps"] != float("inf")):
+        bad.add(E_ARG)
+    # the plain and residual forms are one entry point: residual == NULL selects plain
+    residual = not gate and p["e"] is not None
+    if not gate and not residual and p["h"] is not None:
+        bad.add(E_ARG)  # h_out only with a residual
+    if p["w"] is None:
+        bad.add(E_NULL)
+    if rows > 0:
+        if any(p[k] is None for k in ("x", "y", "rstd")) or (gate and p["e"] is None):
+            bad.add(E_NULL)
+        if residual and p["h"] is None:
+            bad.add(E_NULL)
+    mis = p["w"] is not None and p["w"] % 16
+    if rows > 0:
+        mis = mis or any(p.get(k) is not None and p[k] % 16 for k in ("x", "y", "e", "h"))
+        mis = mis or (p["rstd"] is not None and p["rstd"] % 4)
+    if mis:
+        bad.add(E_ALIGN)
+    ins = [(p[k], n[k]) for k in ("x", "e", "w")]
+    outs = [(p[k], n[k]) for k in ("y", "h", "rstd")]
+    for i, o in enumerate(outs):
+        if any(_overlap(o, b) for b in ins) or any(_overlap(o, b) for j, b in enumerate(outs) if j != i):
+            bad.add(E_ALIAS)
+    return bad
+
+
+@settings(max_examples=800, deadline=None, suppress_health_check=[HealthCheck.too_slow,
+                                                                   HealthCheck.filter_too_much])
+@given(fwd_calls())
+def test_fwd_call_status_follows_the_header_rules(c):
+    import torch
+    if torch.cuda.is_available():
+        return  # a valid call would launch on fake addresses
+    p = c["ptr"]
+    L = R.Layout(c["T"], c["heads"], c["W"], c["xs"][0], c["xs"][1], c["xs"][0], c["xs"][1])
+    if c["form"] == "gate":
+        rc = R.lib().rmsnorm_silu_gate_train_fwd(p["x"], p["e"], p["w"], c["wd"], c["eps"],
+                                                  C.byref(L), p["y"], p["rstd"], None)
+    else:
+        rc = R.lib().rmsnorm_train_fwd(p["x"], p["e"], p["w"], c["wd"], c["eps"], C.byref(L),
+                                       p["y"], p["h"], p["rstd"], None)
+    bad = fwd_broken_rules(c)
+    rows = c["T"] * c["heads"]
+    if bad:
+        assert rc in bad, f"status {rc}, broken rules {sorted(bad)}"
+    elif rows == 0:
+        assert rc == OK  # nothing to enqueue
+    else:
+        assert rc == E_HIP, f"status {rc} for a call that breaks no rule"
