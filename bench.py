@@ -28,8 +28,11 @@ T_HEAD, H_HEAD = 131072, 4096
 # with FP32 weight ("new us" column). Context for vs_baseline, not a target.
 PAGES_BWD_US_B200 = 489.86
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_131072x4096.json")
+# Device code the counters measure; the host-side plan that also decides the
+# bytes (chunk count, grids, workspace) is compared separately, so that edits
+# to validation code elsewhere in the C ABI do not void the counter summary.
 KERNEL_SOURCES = ["rmsn_kernels.hpp", "rmsn_device.hpp", "rmsn_bwd_large.hip", "rmsn_fwd.hip",
-                  "rmsn_launch.hpp", "rmsn_abi.cpp"]
+                  "rmsn_launch.hpp"]
 
 
 def bwd_bytes(T, H, w_bytes):
@@ -49,15 +52,26 @@ def kernel_hash():
     return h.hexdigest()[:16]
 
 
+def headline_plan():
+    """The backward plan of the headline call (host-only query), as a list."""
+    import torch
+
+    import rmsnorm_train_fwd_amd as R
+    x = torch.empty((T_HEAD, H_HEAD), dtype=torch.bfloat16)
+    p = R.rmsnorm_train_bwd_query(x, False)
+    return [p.path, p.chunks, p.subchains, p.fold_group, p.grid, p.fold_grid, p.workspace_bytes]
+
+
 def measured_traffic():
     """HBM bytes per call from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+    was taken on the current kernel sources and the same headline plan; else
+    None."""
     try:
         with open(TRAFFIC_FILE) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_hash") != kernel_hash():
+    if t.get("kernel_hash") != kernel_hash() or t.get("headline_plan") != headline_plan():
         return None
     return t.get("bytes_per_call")
 
@@ -761,7 +775,7 @@ def traffic_report(fetch_dir, write_dir, out_json, out_md):
         gate.append(dict(T=T, fr=gfr, fw=gfw, br=gbr, bw=gbw, alg_f=alg_gf, alg_b=alg_gb,
                          partials=part_b))
     total, alg = kr + kw + fr + fw, bwd_bytes(T_HEAD, H_HEAD, 4)
-    out = {"kernel_hash": kernel_hash(),
+    out = {"kernel_hash": kernel_hash(), "headline_plan": headline_plan(),
            "workload": "rmsnorm_train_bwd non-deterministic [131072,4096] BF16, w FP32",
            "bytes_per_call": round(total), "algorithmic_bytes_per_call": alg,
            "ratio_to_algorithmic": round(total / alg, 5), "fetch_scale": round(ff, 6),
@@ -834,8 +848,10 @@ written, dw), per call, the backward being main kernel + fold:
 |---|---|---|---|---|---|
 {gate_table}
 
-At the headline shape x, dy and dx are each moved once. Kernel sources hash: {out['kernel_hash']} (bench.py reports
-`traffic` only while the current sources hash to this value).
+At the headline shape x, dy and dx are each moved once. Device sources hash: {out['kernel_hash']}
+({", ".join(KERNEL_SOURCES)}); headline plan (path, chunks, sub-chains, fold group, grid, fold
+grid, workspace bytes): {out['headline_plan']}. bench.py reports `traffic` only while both match
+the current sources and plan.
 """
     with open(out_md, "w") as fh:
         fh.write(md)
