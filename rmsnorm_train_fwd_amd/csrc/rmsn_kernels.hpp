@@ -207,8 +207,9 @@ struct RowBatch {
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         asm volatile("" : "+v"(xv[d][v].x), "+v"(xv[d][v].y), "+v"(xv[d][v].z), "+v"(xv[d][v].w));
-        asm volatile("" : "+v"(gv[d][v].x), "+v"(gv[d][v].y), "+v"(gv[d][v].z), "+v"(gv[d][v].w));
-        if constexpr (FORM != kPlain)
+        if constexpr (FORM != kGate)  // the gate's pass 2 reads x only
+          asm volatile("" : "+v"(gv[d][v].x), "+v"(gv[d][v].y), "+v"(gv[d][v].z), "+v"(gv[d][v].w));
+        if constexpr (FORM == kResidual)
           asm volatile("" : "+v"(ev[d][v].x), "+v"(ev[d][v].y), "+v"(ev[d][v].z), "+v"(ev[d][v].w));
       }
     }
@@ -216,7 +217,9 @@ struct RowBatch {
 
   // Pass 1 (per row): the row sum c = sum g*xhat, and the row's dw terms into
   // acc (they do not depend on c, so they are taken while x and dy are
-  // unpacked anyway). Row sum across the row group. Pass 2: dx (+dz), stores.
+  // unpacked anyway); the gate's dz, which does not depend on c either, is
+  // computed and stored here too. Row sum across the row group. Pass 2: dx,
+  // stores.
   // Acc is Dot2 (deterministic: exact dy*x times rstd, or RN(rstd*silu) for
   // the gate), Block8 (dy times xhat [* silu]) or NoDw (dx only).
   template <bool WF32, class Acc>
@@ -225,9 +228,14 @@ struct RowBatch {
                                                 int q, int lane, float* slots, int& parity,
                                                 Acc* acc, bool sync = false) {
     float dot[D];
+    // Gate: g*silu(z) per element, kept from pass 1 for dx in pass 2, so that
+    // pass 2 reads x only and the sigmoid is taken once per element (one FP32
+    // register per element instead of re-unpacking dy and z and a second
+    // exp2 and reciprocal: the gated backward is close to the VALU limit).
+    float gsl[FORM == kGate ? D : 1][FORM == kGate ? E : 1];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      float xf[E], gf[E], sl[E];
+      float xf[E], gf[E], sl[E], sg[E], zz[E];
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         float t[8];
@@ -240,17 +248,38 @@ struct RowBatch {
         if constexpr (FORM == kGate) {
           unpack8(ev[d][v], t);
 #pragma unroll
-          for (int k = 0; k < 8; ++k) sl[v * 8 + k] = t[k] * sigmoid_f(t[k]);
+          for (int k = 0; k < 8; ++k) {
+            zz[v * 8 + k] = t[k];
+            sg[v * 8 + k] = sigmoid_f(t[k]);
+            sl[v * 8 + k] = t[k] * sg[v * 8 + k];
+          }
         }
       }
       float s = 0.0f;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         float g = gf[e] * wr[e];
-        if constexpr (FORM == kGate) g = g * sl[e];
+        if constexpr (FORM == kGate) {
+          g = g * sl[e];
+          gsl[d][e] = g;
+        }
         s = __builtin_fmaf(g, xf[e] * r[d], s);
       }
       dot[d] = s;
+      if constexpr (FORM == kGate) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          float dz[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int e = v * 8 + k;
+            const float xh = xf[e] * r[d];
+            dz[k] = ((gf[e] * xh) * wr[e]) * (sg[e] * (1.0f + zz[e] * (1.0f - sg[e])));
+          }
+          // unconditional, as the dx stores below
+          st16_stream(a.dz + row[d] * H + elem0<G>(v, lane), pack8(dz));
+        }
+      }
       if constexpr (!__is_same(Acc, NoDw)) {
         if (ok[d]) {
 #pragma unroll
@@ -284,19 +313,16 @@ struct RowBatch {
       const float c = dot[d] / (float)H;
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        float xf[8], gf[8], zf[8], out[8], dz[8];
+        float xf[8], gf[8], zf[8], out[8];
         unpack8(xv[d][v], xf);
-        unpack8(gv[d][v], gf);
-        if constexpr (FORM != kPlain) unpack8(ev[d][v], zf);
+        if constexpr (FORM != kGate) unpack8(gv[d][v], gf);
+        if constexpr (FORM == kResidual) unpack8(ev[d][v], zf);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const float xh = xf[k] * r[d];
-          float g = gf[k] * wr[v * 8 + k];
-          if constexpr (FORM == kGate) {
-            const float sg = sigmoid_f(zf[k]);
-            g = g * (zf[k] * sg);
-            dz[k] = ((gf[k] * xh) * wr[v * 8 + k]) * (sg * (1.0f + zf[k] * (1.0f - sg)));
-          }
+          float g;
+          if constexpr (FORM == kGate) g = gsl[d][v * 8 + k];
+          else g = gf[k] * wr[v * 8 + k];
           float dx = r[d] * __builtin_fmaf(-xh, c, g);
           if constexpr (FORM == kResidual) dx = zf[k] + dx;  // grad_h = dh + dx
           out[k] = dx;
@@ -304,9 +330,7 @@ struct RowBatch {
         // Unconditional: a masked entry holds a copy of a real row of the
         // same call (its index was clamped to that row), so it stores the very
         // bytes that row's own pass stores; no branch around the stores.
-        const int64_t o = row[d] * H + elem0<G>(v, lane);
-        st16_stream(a.dx + o, pack8(out));
-        if constexpr (FORM == kGate) st16_stream(a.dz + o, pack8(dz));
+        st16_stream(a.dx + row[d] * H + elem0<G>(v, lane), pack8(out));
       }
     }
   }
