@@ -556,6 +556,11 @@ def sweep(out_path, reps=SWEEP_REPS):
             run_plain("n1", T, 256, "f32", [False, True], heads=heads, rs=rs, hs=hs,
                       label=f"[{T},{heads},256] strides ({rs},{hs},1)")
             torch.cuda.empty_cache()
+    # one GPU's share of the [131072, 4096] call when its rows are split over 4 or 8
+    # GPUs (row-sharded data parallelism; the 2-GPU share is config 3's T = 65537)
+    for T in (32768, 16384):
+        run_plain("e", T, 4096, "f32", [False, True])
+        torch.cuda.empty_cache()
     with open(out_path, "w") as fh:
         fh.write("| cfg | workload | op | us/call | algorithmic GB/s | % of 8 TB/s |\n|---|---|---|---|---|---|\n")
         for cfg, shape, op, us, gbps in rows:
