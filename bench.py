@@ -57,7 +57,7 @@ def headline_plan():
     import torch
 
     import rmsnorm_train_fwd_amd as R
-    x = torch.empty((T_HEAD, H_HEAD), dtype=torch.bfloat16)
+    x = torch.empty((T_HEAD, H_HEAD), dtype=torch.bfloat16, device="meta")  # shape only
     p = R.rmsnorm_train_bwd_query(x, False)
     return [p.path, p.chunks, p.subchains, p.fold_group, p.grid, p.fold_grid, p.workspace_bytes]
 
@@ -762,7 +762,8 @@ def traffic_report(fetch_dir, write_dir, out_json, out_md):
     import rmsnorm_train_fwd_amd as R
 
     def chunks_of(T):
-        return R.rmsnorm_train_bwd_query(torch.empty((T, H_HEAD), dtype=torch.bfloat16),
+        return R.rmsnorm_train_bwd_query(torch.empty((T, H_HEAD), dtype=torch.bfloat16,
+                                                     device="meta"),
                                          False).chunks
 
     chunks = chunks_of(T_HEAD)
