@@ -6,17 +6,19 @@ modes and checks every row and column against the FP64 oracle within the same
 budgets as the configuration tests; a second test requires the deterministic
 dw and dx to keep their bits under three drawn launch overrides (grids of both
 launches, either path), as the deterministic mode promises (PR #8512 page,
-description). The shapes are small enough for the oracle to take well under a
+description), and a third dw in BF16 to be the same value as the FP32 dw
+rounded once (within one BF16 ulp). The shapes are small enough for the oracle to take well under a
 second each.
 """
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import rmsnorm_train_fwd_amd as R
 import synth
 
-from helpers import OnGpu, bits
+from helpers import OnGpu, bf16_ulp_distance, bits
 from test_gpu_parity import run_case
 
 pytestmark = pytest.mark.gpu
@@ -113,3 +115,33 @@ def test_random_case_det_bits_do_not_depend_on_the_launch(c):
         assert np.array_equal(dw, ref_dw), f"det dw bits changed with launch {tag}"
         assert np.array_equal(dx, ref_dx), f"dx bits changed with launch {tag}"
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("c", CASES, ids=_ids)
+def test_random_case_bf16_dw_is_the_same_value_rounded_once(c):
+    # dw_dtype BF16 rounds dw's FP64 value once to BF16, where the FP32 output
+    # rounds it once to FP32: the two agree to one BF16 ulp (zero but at a
+    # BF16 rounding boundary), in both modes. (Against the oracle, the FP32 dw
+    # is checked by the parity test above; the BF16 dw of the exact forms is
+    # pinned to the exact sum, with the oracle's rstd, in test_gpu_det_exact.)
+    p = _problem(c)
+    g = OnGpu(p)
+    zc = dict(zero_centred=c["zero_centred"])
+    launch = None if c["path"] == R.PATH_AUTO else R.Launch(0, 0, c["path"])
+    kw = dict(launch=launch, **zc)
+    if c["form"] == "residual":
+        _, rstd, h = R.rmsnorm_train_fwd(g.x, g.w, p.eps, residual=g.e, **zc)
+        run = lambda m, dt: R.rmsnorm_train_bwd(g.dy, h, rstd, g.w, m, dh=g.dh, dw_dtype=dt, **kw)[1]
+    elif c["form"] == "gate":
+        _, rstd = R.rmsnorm_silu_gate_train_fwd(g.x, g.e, g.w, p.eps, **zc)
+        run = lambda m, dt: R.rmsnorm_silu_gate_train_bwd(g.dy, g.x, g.e, rstd, g.w, m, dw_dtype=dt,
+                                                          **kw)[2]
+    else:
+        _, rstd = R.rmsnorm_train_fwd(g.x, g.w, p.eps, **zc)
+        run = lambda m, dt: R.rmsnorm_train_bwd(g.dy, g.x, rstd, g.w, m, dw_dtype=dt, **kw)[1]
+    for m in (True, False):
+        dw16, dw32 = run(m, torch.bfloat16), run(m, torch.float32)
+        assert dw16.dtype == torch.bfloat16
+        ulp = bf16_ulp_distance(bits(dw16), oracle.f64_to_bf16(dw32.cpu().double().numpy()))
+        assert ulp.max(initial=0) <= 1, (f"BF16 and FP32 dw ({'det' if m else 'nondet'}) differ by "
+                                         f"{ulp.max()} BF16 ulp")
